@@ -1,0 +1,15 @@
+"""CPU oracle for the exact attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The product path (the HIP library
+and its Python binding) never calls it and shares no code with it.
+"""
+
+from .attention import (  # noqa: F401
+    attention,
+    attention_blocked,
+    attention_bruteforce,
+    online_softmax_ul,
+    online_softmax_normalised,
+    row_probabilities,
+)
