@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of libmi_attn's attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one forward pass (one kernel launch) over the whole workload, with
+Q, K, V and the outputs resident in HBM.  The K timed steps are captured
+back-to-back in one HIP graph and replayed between two HIP events recorded
+on the stream the kernels run on, so launch overhead on the host is not in
+the figure; `ms_per_step_eager` gives the plain per-call rate for context.
+
+Prints one JSON line.  `value` is algorithmic TFLOP/s of the workload:
+4 * d * Hq * (visible query/key pairs) per forward.  `roofline` relates the
+kernel to the dense fp16/bf16 MFMA peak of MI355X; `traffic` comes from
+rocprofv3 counters committed under profiles/ and is reported only while the
+kernel source still hashes to the value recorded with them.  `cpu_baseline`
+times the fp64 CPU oracle on the host cores over the same workload and also
+yields the parity errors of this run's GPU output.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}   # MI355X dense MFMA, per GPU
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_61_amd", "csrc",
+                          "attn_fwd_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_mfma_traffic.json")
+
+
+def visible_pairs(w, lengths=None):
+    """Number of (query, key) pairs a forward pass must combine, per head."""
+    if w.varlen:
+        pairs = 0
+        for n in lengths:
+            pairs += n * (n + 1) // 2 if w.causal else n * n
+        return pairs
+    lq, lk = w.lq, w.lk
+    if not w.causal:
+        return w.batch * lq * lk
+    per = sum(min(lk, max(0, i + lk - lq + 1)) for i in range(lq))
+    return w.batch * per
+
+
+def algorithmic_bytes(w, inp):
+    """Q, K, V read once and O, LSE written once."""
+    esz = {"f16": 2, "bf16": 2, "f32": 4}
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    n_in = (q.numel() + k.numel() + v.numel()) * esz[w.in_dtype]
+    rows = q.numel() // w.d
+    return n_in + rows * w.d * esz[w.out_dtype] + rows * 4
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per launch from the committed counter summary, or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha256_16") != kernel_hash():
+        return None
+    ent = rec.get("workloads", {}).get(workload)
+    if not ent:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info()
+             if i.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, inp, o_gpu, lse_gpu, flops):
+    """Time the fp64 oracle over the whole workload; also return parity."""
+    import numpy as np
+    import oracle
+    import workloads
+    f64 = workloads.to_f64
+    args = (f64(inp["q"]), f64(inp["k"]), f64(inp["v"]))
+    t0 = time.perf_counter()
+    o_ref, l_ref = oracle.attention(*args, scale=w.scale, causal=w.causal,
+                                    cu_seqlens_q=inp.get("cu_seqlens_q"),
+                                    cu_seqlens_k=inp.get("cu_seqlens_k"))
+    dt = time.perf_counter() - t0
+    err_o = float(np.max(np.abs(o_gpu - o_ref)))
+    live = np.isfinite(l_ref)
+    err_l = float(np.max(np.abs(lse_gpu[live] - l_ref[live])))
+    dead_ok = bool(np.all(lse_gpu[~live] == -math.inf))
+    base = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"the whole {w.name} workload once, fp64 numpy "
+                      f"(S and P materialised per head in 1024-row chunks), "
+                      f"{dt:.2f} s"}
+    parity = {"max_abs_err_o": err_o, "max_abs_err_lse": err_l,
+              "dead_rows_exact": dead_ok,
+              "pass": err_o <= 1e-2 and err_l <= 1e-3 and dead_ok}
+    return base, parity
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): "
+              "attention over independent (batch, head) pairs would shard "
+              "with no exchange, and no multi-GPU figure is produced.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import exact_attention_61_amd as mi
+
+    name = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make(name, seed=0)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    kw = dict(causal=w.causal, scale=w.scale)
+    out_dtype = workloads.DTYPES[w.out_dtype]
+    o = torch.empty(q.shape, dtype=out_dtype, device=dev)
+    if w.varlen:
+        kw.update(cu_seqlens_q=inp["cu_seqlens_q"].to(dev),
+                  cu_seqlens_k=inp["cu_seqlens_k"].to(dev),
+                  max_seqlen_q=inp["max_seqlen_q"],
+                  max_seqlen_k=inp["max_seqlen_k"])
+        lse = torch.empty((w.hq, q.shape[0]), dtype=torch.float32, device=dev)
+    else:
+        lse = torch.empty((w.batch, w.hq, w.lq), dtype=torch.float32,
+                          device=dev)
+
+    def step():
+        mi.mi_attn_fwd(q, k, v, o, lse, **kw)
+
+    lengths = inp.get("lengths")
+    flops = 4.0 * w.d * w.hq * visible_pairs(w, lengths)
+    nbytes = algorithmic_bytes(w, inp)
+
+    # warm-up (eager), then capture K back-to-back launches in one graph
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            step()
+    graph.replay()                       # warm replay
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms = ms_total / args.steps
+
+    # plain eager calls, for context
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.in_dtype]
+    props = torch.cuda.get_device_properties(dev)
+    traffic = load_traffic(name)
+
+    o_gpu = o.to("cpu", torch.float64).numpy()
+    lse_gpu = lse.to("cpu", torch.float64).numpy()
+    base, parity = (None, None)
+    if not args.no_cpu_baseline:
+        base, parity = cpu_baseline(w, inp, o_gpu, lse_gpu, flops)
+
+    rec = {
+        "metric": "attn fwd TFLOP/s + % of fp16 MFMA peak, B2 H16 N2048 d64 "
+                  "causal",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.in_dtype,
+        "data": "synthetic (seeded N(0,1))",
+        "config": {"workload": name, "batch": w.batch, "hq": w.hq,
+                   "hkv": w.hkv, "lq": w.lq, "lk": w.lk, "head_dim": w.d,
+                   "causal": w.causal, "varlen": w.varlen,
+                   "in_dtype": w.in_dtype, "out_dtype": w.out_dtype,
+                   "lengths": lengths},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "algorithmic_flops": flops,
+        # the common convention: 4*B*H*Lq*Lk*d, halved for causal
+        "flops_common_convention": (2.0 if w.causal else 4.0) * w.batch *
+        w.hq * w.lq * w.lk * w.d,
+        "ms_per_step_eager": round(ms_eager, 6),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes": nbytes,
+                     "kernel": "attn_fwd_mfma_kernel"},
+        "cpu_baseline": base,
+        "parity": parity,
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "gcn_arch": getattr(props, "gcnArchName", None)},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+"""Python binding of libmi_attn (exact attention forward for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  PyTorch supplies device memory and the current stream.  If the
+shared library has not been built, importing this package raises.
+
+Entry points mirror the C ABI of include/mi_attn.h:
+
+* mi_attn_fwd(q, k, v, o, lse, ...)  -- writes into caller-provided tensors;
+* mi_attn_status_string(code), mi_attn_version(), mi_attn_last_hip_error();
+
+plus forward(q, k, v, ...) -> (out, lse), which allocates the outputs.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmi_attn.so")
+
+MI_ATTN_F16, MI_ATTN_BF16, MI_ATTN_F32 = 0, 1, 2
+_DTYPE_CODE = {torch.float16: MI_ATTN_F16, torch.bfloat16: MI_ATTN_BF16,
+               torch.float32: MI_ATTN_F32}
+
+STATUS_NAMES = {0: "MI_ATTN_OK", 1: "MI_ATTN_ERR_NULL", 2: "MI_ATTN_ERR_SHAPE",
+                3: "MI_ATTN_ERR_LAYOUT", 4: "MI_ATTN_ERR_DTYPE",
+                5: "MI_ATTN_ERR_UNSUPPORTED", 6: "MI_ATTN_ERR_ARG",
+                7: "MI_ATTN_ERR_HIP"}
+
+
+class Strides(ctypes.Structure):
+    """mi_attn_strides_t: element strides of a [batch, head, row, col] view."""
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64),
+                ("row", ctypes.c_int64)]
+
+
+class MiAttnError(RuntimeError):
+    def __init__(self, status, detail=""):
+        self.status = status
+        msg = mi_attn_status_string(status)
+        if detail:
+            msg += f" ({detail})"
+        super().__init__(msg)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libmi_attn.so is not built ({LIB_PATH} missing); run "
+            "`python -m exact_attention_61_amd.build` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    S = ctypes.POINTER(Strides)
+    i32 = ctypes.c_int32
+    lib.mi_attn_fwd.restype = ctypes.c_int
+    lib.mi_attn_fwd.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int,
+                                i32, i32, i32, i32, i32, i32, S, S, S, S, P, P,
+                                ctypes.c_float, i32, P]
+    lib.mi_attn_status_string.restype = ctypes.c_char_p
+    lib.mi_attn_status_string.argtypes = [ctypes.c_int]
+    lib.mi_attn_version.restype = i32
+    lib.mi_attn_version.argtypes = []
+    lib.mi_attn_last_hip_error.restype = i32
+    lib.mi_attn_last_hip_error.argtypes = []
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    """The loaded ctypes library (raw C entry points)."""
+    return _lib
+
+
+def mi_attn_status_string(status):
+    return _lib.mi_attn_status_string(int(status)).decode()
+
+
+def mi_attn_version():
+    return int(_lib.mi_attn_version())
+
+
+def mi_attn_last_hip_error():
+    return int(_lib.mi_attn_last_hip_error())
+
+
+def _strides(t, layout, packed):
+    """Element strides (batch, head, row) of q/k/v/o as the ABI wants them."""
+    if t.stride(-1) != 1:
+        raise MiAttnError(3, "last dimension must be contiguous")
+    st = t.stride()
+    if packed:                      # [T, H, d]
+        return Strides(0, st[1], st[0])
+    if layout == "bhsd":            # [B, H, L, d]
+        return Strides(st[0], st[1], st[2])
+    if layout == "bshd":            # [B, L, H, d]
+        return Strides(st[0], st[2], st[1])
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def _dims(q, k, layout, packed):
+    if packed:
+        return 0, q.shape[1], k.shape[1], q.shape[0], k.shape[0]
+    if layout == "bhsd":
+        return q.shape[0], q.shape[1], k.shape[1], q.shape[2], k.shape[2]
+    return q.shape[0], q.shape[2], k.shape[2], q.shape[1], k.shape[1]
+
+
+def _ptr(t):
+    if t is None or t.numel() == 0:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def mi_attn_fwd(q, k, v, o, lse=None, *, causal=False, scale=None,
+                cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                max_seqlen_k=None, layout="bhsd", stream=None):
+    """Call the C entry point on caller-provided tensors (all on one device).
+
+    Dense q is [B, Hq, Lq, d] ("bhsd") or [B, Lq, Hq, d] ("bshd"); packed q is
+    [Tq, Hq, d] with int32 cu_seqlens_q / cu_seqlens_k of length B + 1 and
+    max_seqlen_q / max_seqlen_k.  lse (float32) is [B, Hq, Lq] dense or
+    [Hq, Tq] packed, or None.  scale=None means 1/sqrt(head_dim).
+    """
+    packed = cu_seqlens_q is not None or cu_seqlens_k is not None
+    for t in (q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k):
+        if t is not None and (not t.is_cuda or t.device != q.device):
+            raise MiAttnError(6, "every tensor must be on q's GPU device")
+    if q.dtype not in _DTYPE_CODE or o.dtype not in _DTYPE_CODE:
+        raise MiAttnError(4, f"{q.dtype} -> {o.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise MiAttnError(4, "q, k and v must share one dtype")
+    d = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    bsz, hq, hkv, lq, lk = _dims(q, k, layout, packed)
+    if packed:
+        if cu_seqlens_q is None or cu_seqlens_k is None:
+            raise MiAttnError(6, "give both cu_seqlens_q and cu_seqlens_k")
+        bsz = cu_seqlens_q.numel() - 1
+        lq = int(max_seqlen_q)
+        lk = int(max_seqlen_k)
+        for cu in (cu_seqlens_q, cu_seqlens_k):
+            if cu.dtype != torch.int32 or not cu.is_contiguous():
+                raise MiAttnError(3, "cu_seqlens must be contiguous int32")
+        if os.environ.get("MI_ATTN_DEBUG") == "1":
+            _check_cu(cu_seqlens_q, lq, q.shape[0])
+            _check_cu(cu_seqlens_k, lk, k.shape[0])
+    if lse is not None and (lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise MiAttnError(3, "lse must be contiguous float32")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    qs, ks, vs, os_ = (_strides(t, layout, packed) for t in (q, k, v, o))
+    st = _lib.mi_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+        _DTYPE_CODE[q.dtype], _DTYPE_CODE[o.dtype],
+        bsz, hq, hkv, lq, lk, d,
+        ctypes.byref(qs), ctypes.byref(ks), ctypes.byref(vs),
+        ctypes.byref(os_), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+        float(scale), int(bool(causal)), ctypes.c_void_p(stream))
+    if st != 0:
+        detail = ""
+        if st == 7:
+            detail = f"hipError {mi_attn_last_hip_error()}"
+        raise MiAttnError(st, detail)
+
+
+def _check_cu(cu, max_len, rows):
+    """Host-side check of a cu_seqlens array (only with MI_ATTN_DEBUG=1)."""
+    c = cu.to("cpu").tolist()
+    if c[0] != 0:
+        raise MiAttnError(6, "cu_seqlens[0] must be 0")
+    for a, b in zip(c, c[1:]):
+        if b < a or b - a > max_len:
+            raise MiAttnError(6, "cu_seqlens must be non-decreasing with "
+                                 "lengths <= max_seqlen")
+    if c[-1] > rows:
+        raise MiAttnError(6, "cu_seqlens points past the tensor")
+
+
+def forward(q, k, v, *, causal=False, scale=None, cu_seqlens_q=None,
+            cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
+            out_dtype=None, layout="bhsd", return_lse=True):
+    """Allocate out (and lse) and run mi_attn_fwd; returns (out, lse)."""
+    packed = cu_seqlens_q is not None or cu_seqlens_k is not None
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    lse = None
+    if return_lse:
+        if packed:
+            lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32,
+                              device=q.device)
+        else:
+            bsz, hq, _, lq, _ = _dims(q, k, layout, packed)
+            lse = torch.empty((bsz, hq, lq), dtype=torch.float32,
+                              device=q.device)
+    with torch.cuda.device(q.device):
+        mi_attn_fwd(q, k, v, out, lse, causal=causal, scale=scale,
+                    cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
+                    max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+                    layout=layout)
+    return out, lse

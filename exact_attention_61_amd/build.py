@@ -1,0 +1,75 @@
+"""Build libmi_attn.so in-tree with hipcc for gfx950.
+
+Usage: python -m exact_attention_61_amd.build   (or build() from Python).
+Every .hip file under csrc/ is compiled to an object in _build/ and linked
+into exact_attention_61_amd/libmi_attn.so.  It always recompiles.
+"""
+
+import concurrent.futures as cf
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libmi_attn.so")
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-fvisibility=hidden",
+    "-Wall",
+    "-Wno-unused-function",
+    # no packed fp32 instructions anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _hipcc():
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"),
+                 "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libmi_attn)")
+
+
+def _run(cmd):
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("command failed: " + " ".join(cmd) + "\n" +
+                           res.stdout + res.stderr)
+    return res
+
+
+def build(verbose=False, extra_flags=()):
+    """Compile every csrc/*.hip and link libmi_attn.so; return its path."""
+    hipcc = _hipcc()
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    jobs = max(1, min(len(srcs), os.cpu_count() or 1, 8))
+    cmds = [[hipcc, *HIPCC_FLAGS, *extra_flags, "-c", s, "-o", o]
+            for s, o in zip(srcs, objs)]
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        for cmd, _ in zip(cmds, ex.map(_run, cmds)):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+          *objs])
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB, flush=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-q" not in sys.argv)

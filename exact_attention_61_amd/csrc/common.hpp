@@ -1,0 +1,80 @@
+// Shared definitions of libmi_attn's kernels and host launcher (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi_attn {
+
+// Everything a forward kernel needs, passed by value as the kernel argument.
+// Offsets are in elements.  For packed variable-length input the batch
+// strides are unused and row r of sequence b lives at row cu[b] + r.
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;                 // may be null
+    const int32_t* cu_q;        // null for dense input
+    const int32_t* cu_k;
+    int64_t q_sb, q_sh, q_sr;
+    int64_t k_sb, k_sh, k_sr;
+    int64_t v_sb, v_sh, v_sr;
+    int64_t o_sb, o_sh, o_sr;
+    int32_t batch, hq, hkv, group;   // group = hq / hkv
+    int32_t lq, lk;                  // dense lengths, or the packed maxima
+    float scale_log2;                // |scale| * log2(e), in fp32
+    int32_t negate_q;                // 1 when scale < 0 (fold the sign into q)
+    int32_t causal;
+};
+
+// Storage tags for the element types (16-bit values are kept as raw bits).
+struct f16_t { uint16_t bits; };
+struct bf16_t { uint16_t bits; };
+
+__device__ __forceinline__ float to_f32(f16_t x) {
+    return (float)__builtin_bit_cast(_Float16, x.bits);
+}
+__device__ __forceinline__ float to_f32(bf16_t x) {
+    return __builtin_bit_cast(float, (uint32_t)x.bits << 16);
+}
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct OutStore;
+template <> struct OutStore<f16_t> {
+    __device__ __forceinline__ static void put(void* base, int64_t i, float x) {
+        reinterpret_cast<uint16_t*>(base)[i] = f32_to_f16_bits(x);
+    }
+};
+template <> struct OutStore<bf16_t> {
+    __device__ __forceinline__ static void put(void* base, int64_t i, float x) {
+        reinterpret_cast<uint16_t*>(base)[i] = f32_to_bf16_bits(x);
+    }
+};
+template <> struct OutStore<float> {
+    __device__ __forceinline__ static void put(void* base, int64_t i, float x) {
+        reinterpret_cast<float*>(base)[i] = x;
+    }
+};
+
+// Host-side launchers, one per kernel family.  They only launch: every
+// argument was validated by the caller.  Return the hipGetLastError() code.
+hipError_t launch_simple(const FwdParams& p, int in_dtype, int out_dtype,
+                         int head_dim, hipStream_t stream);
+hipError_t launch_mfma(const FwdParams& p, int in_dtype, int out_dtype,
+                       int head_dim, hipStream_t stream);
+
+}  // namespace mi_attn

@@ -1,0 +1,160 @@
+// Host side of libmi_attn: the C ABI declared in include/mi_attn.h.
+//
+// Every argument is validated before the first HIP call, so a rejected call
+// enqueues nothing and touches no output.  Validation mirrors the input
+// checks of the pages' fused-dense binding (dtype, contiguity and shape
+// checks before any launch, an error code instead of a crash) and the
+// training tutorial's constraints (Hkv divides Hq, head_dim a multiple of 8).
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/mi_attn.h"
+#include "common.hpp"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+bool aligned16(const void* p) {
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+bool stride_ok(const mi_attn_strides_t& s) {
+    return s.batch >= 0 && s.head >= 0 && s.row >= 0 && s.batch % 8 == 0 &&
+           s.head % 8 == 0 && s.row % 8 == 0;
+}
+
+// MI_ATTN_KERNEL=simple selects the scalar kernel (a second, independent
+// implementation kept for cross-checks); anything else runs the MFMA kernel.
+bool use_scalar_kernel() {
+    static const bool v = [] {
+        const char* e = std::getenv("MI_ATTN_KERNEL");
+        return e != nullptr && std::strcmp(e, "simple") == 0;
+    }();
+    return v;
+}
+
+mi_attn_strides_t default_strides(bool packed, int64_t heads, int64_t rows,
+                                  int64_t d) {
+    if (packed) return mi_attn_strides_t{0, d, heads * d};
+    return mi_attn_strides_t{heads * rows * d, rows * d, d};
+}
+
+}  // namespace
+
+extern "C" {
+
+mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
+                             void* o, float* lse, mi_attn_dtype_t in_dtype,
+                             mi_attn_dtype_t out_dtype, int32_t batch,
+                             int32_t hq, int32_t hkv, int32_t lq, int32_t lk,
+                             int32_t head_dim, const mi_attn_strides_t* q_strides,
+                             const mi_attn_strides_t* k_strides,
+                             const mi_attn_strides_t* v_strides,
+                             const mi_attn_strides_t* o_strides,
+                             const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k, float scale,
+                             int32_t causal, struct ihipStream_t* stream) {
+    if (in_dtype != MI_ATTN_F16 && in_dtype != MI_ATTN_BF16)
+        return MI_ATTN_ERR_DTYPE;
+    if (out_dtype != in_dtype && out_dtype != MI_ATTN_F32)
+        return MI_ATTN_ERR_DTYPE;
+    if (batch < 0 || lq < 0 || lk < 0 || hq < 1 || hkv < 1 || hq % hkv != 0)
+        return MI_ATTN_ERR_SHAPE;
+    // Launch-size limits: work-groups along each grid axis stay below 2^31.
+    if (hq > 65535 || batch > 65535) return MI_ATTN_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return MI_ATTN_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale)) return MI_ATTN_ERR_ARG;
+    if (causal != 0 && causal != 1) return MI_ATTN_ERR_ARG;
+    const bool packed = cu_seqlens_q != nullptr;
+    if (packed != (cu_seqlens_k != nullptr)) return MI_ATTN_ERR_ARG;
+    if (batch == 0 || lq == 0) return MI_ATTN_OK;   // nothing to compute
+    // K and V may be absent only when a dense call has no key rows at all.
+    const bool no_keys = !packed && lk == 0;
+    if (q == nullptr || o == nullptr ||
+        (!no_keys && (k == nullptr || v == nullptr)))
+        return MI_ATTN_ERR_NULL;
+
+    const mi_attn_strides_t qs =
+        q_strides ? *q_strides : default_strides(packed, hq, lq, head_dim);
+    const mi_attn_strides_t ks =
+        k_strides ? *k_strides : default_strides(packed, hkv, lk, head_dim);
+    const mi_attn_strides_t vs =
+        v_strides ? *v_strides : default_strides(packed, hkv, lk, head_dim);
+    const mi_attn_strides_t os =
+        o_strides ? *o_strides : default_strides(packed, hq, lq, head_dim);
+    if (!stride_ok(qs) || !stride_ok(ks) || !stride_ok(vs) || !stride_ok(os))
+        return MI_ATTN_ERR_LAYOUT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
+        return MI_ATTN_ERR_LAYOUT;
+
+    mi_attn::FwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.q_sb = qs.batch; p.q_sh = qs.head; p.q_sr = qs.row;
+    p.k_sb = ks.batch; p.k_sh = ks.head; p.k_sr = ks.row;
+    p.v_sb = vs.batch; p.v_sh = vs.head; p.v_sr = vs.row;
+    p.o_sb = os.batch; p.o_sh = os.head; p.o_sr = os.row;
+    p.batch = batch;
+    p.hq = hq;
+    p.hkv = hkv;
+    p.group = hq / hkv;
+    p.lq = lq;
+    p.lk = lk;
+    // |scale| * log2(e), floored at 1e-30 so that a masked score (-inf) times
+    // the factor stays -inf; a smaller factor changes no visible score.
+    p.scale_log2 = (float)std::fmax(
+        std::fabs((double)scale) * 1.4426950408889634074, 1e-30);
+    p.negate_q = scale < 0.0f ? 1 : 0;
+    p.causal = causal;
+
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const hipError_t err =
+        use_scalar_kernel()
+            ? mi_attn::launch_simple(p, (int)in_dtype, (int)out_dtype,
+                                     head_dim, st)
+            : mi_attn::launch_mfma(p, (int)in_dtype, (int)out_dtype, head_dim,
+                                   st);
+    if (err != hipSuccess) {
+        g_last_hip_error = (int32_t)err;
+        return MI_ATTN_ERR_HIP;
+    }
+    return MI_ATTN_OK;
+}
+
+const char* mi_attn_status_string(mi_attn_status_t status) {
+    switch (status) {
+        case MI_ATTN_OK: return "MI_ATTN_OK: success";
+        case MI_ATTN_ERR_NULL: return "MI_ATTN_ERR_NULL: q, k, v or o is NULL";
+        case MI_ATTN_ERR_SHAPE:
+            return "MI_ATTN_ERR_SHAPE: negative size, Hq/Hkv < 1, Hq not a "
+                   "multiple of Hkv, or size beyond the launch limits";
+        case MI_ATTN_ERR_LAYOUT:
+            return "MI_ATTN_ERR_LAYOUT: pointer not 16-byte aligned or stride "
+                   "negative / not a multiple of 8 elements";
+        case MI_ATTN_ERR_DTYPE:
+            return "MI_ATTN_ERR_DTYPE: inputs must be F16 or BF16 and the "
+                   "output the input type or F32";
+        case MI_ATTN_ERR_UNSUPPORTED:
+            return "MI_ATTN_ERR_UNSUPPORTED: head_dim must be 64 or 128";
+        case MI_ATTN_ERR_ARG:
+            return "MI_ATTN_ERR_ARG: scale not finite, causal not 0/1, or only "
+                   "one cu_seqlens pointer given";
+        case MI_ATTN_ERR_HIP: return "MI_ATTN_ERR_HIP: kernel launch failed";
+    }
+    return "unknown mi_attn status";
+}
+
+int32_t mi_attn_version(void) { return MI_ATTN_ABI_VERSION; }
+
+int32_t mi_attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

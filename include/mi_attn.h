@@ -1,0 +1,155 @@
+/*
+ * mi_attn.h — C ABI of libmi_attn, an exact attention forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the call computes.  For every batch entry b and query head h, with
+ * key/value head g = floor(h / (Hq / Hkv)):
+ *
+ *     S[i, j] = scale * sum_c Q[b, h, i, c] * K[b, g, j, c]
+ *     P[i, :] = softmax over the keys j visible to query i
+ *     O[b, h, i, :] = sum_j P[i, j] * V[b, g, j, :]
+ *     LSE[b, h, i]  = ln sum_j exp(S[i, j])            (visible j only)
+ *
+ * This is standard attention as stated on the fusion/compiler notes page
+ * ("FlashAttention: turning the quadratic intermediate matrices into
+ * statistics", clxhxhhr.top post 5544, section 3), computed tile by tile with
+ * the online-softmax statistics of its section 3.1 (running max m, rescaled
+ * exp-sum l, rescaled output accumulator), so no Lq x Lk score or probability
+ * matrix is ever written to memory.  The interface follows the training
+ * integration tutorial (inference.lei6393.com, sections 2.2-2.5 and 8.5):
+ * causal masking, grouped-query attention with Hkv dividing Hq, cross
+ * attention with Lq != Lk, packed variable-length batches in place of a
+ * key padding mask, and a default scale of 1/sqrt(head_dim) (applied by the
+ * Python binding; this C call always takes the scale explicitly).
+ *
+ * Visibility.  Key j of a sequence is visible to query i of the same sequence
+ * iff j < Lk_b and, when causal != 0, j <= i + Lk_b - Lq_b (bottom-right
+ * alignment: with Lq == Lk this is j <= i).  A query row with no visible key
+ * gets O = 0 and LSE = -inf.
+ *
+ * Ownership and threading.  The caller owns every buffer.  The library never
+ * allocates, frees or keeps a pointer past the call, holds no mutable global
+ * state and may be called from several threads at once.  The work is
+ * enqueued on `stream` on the current HIP device and the call returns at
+ * once; buffers must stay alive until that stream work is done.
+ */
+#ifndef MI_ATTN_H
+#define MI_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MI_ATTN_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MI_ATTN_API __attribute__((visibility("default")))
+#else
+#define MI_ATTN_API
+#endif
+
+/* Return codes.  Every argument is checked on the host before any HIP call;
+ * on any error nothing is enqueued and o / lse are left untouched. */
+typedef enum mi_attn_status {
+    MI_ATTN_OK = 0,
+    MI_ATTN_ERR_NULL = 1,        /* q, k, v or o is NULL where rows exist     */
+    MI_ATTN_ERR_SHAPE = 2,       /* negative size, Hq or Hkv < 1,
+                                    Hq % Hkv != 0, size too large            */
+    MI_ATTN_ERR_LAYOUT = 3,      /* pointer not 16-byte aligned, stride not a
+                                    multiple of 8 elements or negative        */
+    MI_ATTN_ERR_DTYPE = 4,       /* in dtype not F16/BF16, or out dtype not
+                                    the in dtype or F32                       */
+    MI_ATTN_ERR_UNSUPPORTED = 5, /* head_dim not 64 or 128                    */
+    MI_ATTN_ERR_ARG = 6,         /* scale not finite, causal not 0/1, only
+                                    one of the cu_seqlens pointers given      */
+    MI_ATTN_ERR_HIP = 7          /* the kernel launch failed (the HIP error
+                                    is kept per thread, see below)            */
+} mi_attn_status_t;
+
+/* Element types. */
+typedef enum mi_attn_dtype {
+    MI_ATTN_F16 = 0,
+    MI_ATTN_BF16 = 1,
+    MI_ATTN_F32 = 2
+} mi_attn_dtype_t;
+
+/* Element strides of a 4-D view [batch, head, row, column]; the column
+ * stride is always 1.  Dense [B, H, L, d] contiguous is
+ * {H*L*d, L*d, d}; [B, L, H, d] (sequence-major) is {L*H*d, d, H*d}.
+ * For packed variable-length tensors [T, H, d] only head and row are used
+ * (row = token) and batch is ignored: {0, d, H*d} when contiguous. */
+typedef struct mi_attn_strides {
+    int64_t batch;
+    int64_t head;
+    int64_t row;
+} mi_attn_strides_t;
+
+struct ihipStream_t;   /* hipStream_t; NULL is the default stream */
+
+/*
+ * mi_attn_fwd — O = softmax(scale * Q K^T, masked) V and LSE, forward only.
+ *
+ * q, k, v   device pointers, element type in_dtype.
+ *           Dense:  q [B, Hq, Lq, d], k and v [B, Hkv, Lk, d] as strided views.
+ *           Packed: q [Tq, Hq, d], k and v [Tk, Hkv, d]; sequence b owns
+ *           query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows
+ *           cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1.
+ * o         device pointer, element type out_dtype, same shape as q (head_dim
+ *           columns), written through o_strides.
+ * lse       device pointer to float, or NULL to skip it.  Dense: contiguous
+ *           [B, Hq, Lq].  Packed: contiguous [Hq, Tq] with Tq =
+ *           cu_seqlens_q[B].  Natural log, scale included.
+ * in_dtype  MI_ATTN_F16 or MI_ATTN_BF16 (q, k and v alike).
+ * out_dtype in_dtype or MI_ATTN_F32 (rounded to nearest even from fp32).
+ * batch     B >= 0.  B == 0 (or Lq == 0) is a no-op that returns MI_ATTN_OK
+ *           once the dtypes and sizes are valid; the pointers may then be
+ *           NULL.  k and v may also be NULL for a dense call with Lk == 0.
+ * hq, hkv   query and key/value heads, hkv >= 1, hq a multiple of hkv.
+ * lq, lk    dense: sequence lengths (>= 0); packed: the longest query / key
+ *           sequence (max_seqlen), used to size the launch.
+ * head_dim  64 or 128.
+ * *_strides element strides (see mi_attn_strides_t); NULL means contiguous
+ *           ([B, H, L, d] dense, [T, H, d] packed).  Strides must be >= 0 and
+ *           multiples of 8; base pointers must be 16-byte aligned.
+ * cu_seqlens_q, cu_seqlens_k  device int32 arrays of B + 1 offsets, both NULL
+ *           (dense) or both set (packed).  Their contents are not checked:
+ *           the caller guarantees cu[0] = 0, non-decreasing, every length
+ *           <= lq (resp. lk), and rows inside the tensors.
+ * scale     multiplies Q K^T; any finite value.
+ * causal    0 or 1 (bottom-right aligned, see above).
+ * stream    HIP stream to enqueue on.
+ *
+ * Returns MI_ATTN_OK once the kernel is enqueued.  Faults inside the kernel
+ * show up at the caller's next synchronisation, as with any HIP launch.
+ */
+MI_ATTN_API mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
+                             void* o, float* lse,
+                             mi_attn_dtype_t in_dtype, mi_attn_dtype_t out_dtype,
+                             int32_t batch, int32_t hq, int32_t hkv,
+                             int32_t lq, int32_t lk, int32_t head_dim,
+                             const mi_attn_strides_t* q_strides,
+                             const mi_attn_strides_t* k_strides,
+                             const mi_attn_strides_t* v_strides,
+                             const mi_attn_strides_t* o_strides,
+                             const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k,
+                             float scale, int32_t causal,
+                             struct ihipStream_t* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+MI_ATTN_API const char* mi_attn_status_string(mi_attn_status_t status);
+
+/* MI_ATTN_ABI_VERSION of the loaded library. */
+MI_ATTN_API int32_t mi_attn_version(void);
+
+/* The hipError_t of the last MI_ATTN_ERR_HIP returned on this thread, 0 if
+ * none. */
+MI_ATTN_API int32_t mi_attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI_ATTN_H */

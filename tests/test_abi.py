@@ -1,0 +1,108 @@
+"""libmi_attn C ABI, checked on the host (no GPU needed).
+
+The library must load, export every function include/mi_attn.h declares, and
+reject every invalid argument with its status code before any HIP call, so
+these calls never reach a device.  Pointers here are fake aligned addresses:
+no call in this file passes validation with rows to compute.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import exact_attention_61_amd as mi
+from exact_attention_61_amd import Strides
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include",
+                      "mi_attn.h")
+
+
+def _header():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def test_exports_every_declared_function():
+    names = re.findall(r"MI_ATTN_API\s+[\w\s\*]+?\b(mi_attn_\w+)\s*\(",
+                       _header())
+    assert set(names) == {"mi_attn_fwd", "mi_attn_status_string",
+                          "mi_attn_version", "mi_attn_last_hip_error"}
+    for n in names:
+        assert hasattr(mi.lib(), n), n
+
+
+def test_version_matches_header():
+    m = re.search(r"#define MI_ATTN_ABI_VERSION (\d+)", _header())
+    assert mi.mi_attn_version() == int(m.group(1))
+
+
+def test_enum_values_match_header():
+    h = _header()
+    for code, name in mi.STATUS_NAMES.items():
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", h), name
+    for name, code in (("MI_ATTN_F16", 0), ("MI_ATTN_BF16", 1),
+                       ("MI_ATTN_F32", 2)):
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", h)
+
+
+def test_status_strings():
+    for code, name in mi.STATUS_NAMES.items():
+        assert mi.mi_attn_status_string(code).startswith(name)
+    assert "unknown" in mi.mi_attn_status_string(99)
+    assert mi.mi_attn_last_hip_error() == 0
+
+
+A = 0x10000          # fake 16-byte-aligned addresses (never dereferenced)
+
+
+def call(q=A, k=A * 2, v=A * 3, o=A * 4, lse=A * 5, in_dt=0, out_dt=0,
+         b=1, hq=2, hkv=1, lq=16, lk=16, d=64, qs=None, ks=None, vs=None,
+         os_=None, cuq=None, cuk=None, scale=0.125, causal=0):
+    ref = lambda s: None if s is None else ctypes.byref(s)
+    return mi.lib().mi_attn_fwd(q, k, v, o, lse, in_dt, out_dt, b, hq, hkv,
+                                lq, lk, d, ref(qs), ref(ks), ref(vs),
+                                ref(os_), cuq, cuk, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(in_dt=2), 4), (dict(in_dt=3), 4), (dict(in_dt=-1), 4),
+    (dict(in_dt=0, out_dt=1), 4), (dict(in_dt=1, out_dt=0), 4),
+    (dict(b=-1), 2), (dict(lq=-1), 2), (dict(lk=-5), 2), (dict(hq=0), 2),
+    (dict(hkv=0), 2), (dict(hq=6, hkv=4), 2), (dict(hq=70000, hkv=1), 2),
+    (dict(d=32), 5), (dict(d=96), 5), (dict(d=256), 5), (dict(d=0), 5),
+    (dict(scale=math.nan), 6), (dict(scale=math.inf), 6),
+    (dict(scale=-math.inf), 6), (dict(causal=2), 6), (dict(causal=-1), 6),
+    (dict(cuq=A * 6), 6), (dict(cuk=A * 6), 6),
+    (dict(q=A + 8), 3), (dict(k=A + 2), 3), (dict(o=A + 4), 3),
+    (dict(lse=A + 2), 3),
+    (dict(qs=Strides(2048, 1024, 63)), 3),
+    (dict(ks=Strides(2048, 1020, 64)), 3),
+    (dict(vs=Strides(-2048, 1024, 64)), 3),
+    (dict(os_=Strides(2048, 1024, -64)), 3),
+])
+def test_rejected_before_any_hip_call(kw, code):
+    assert call(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(b=0), dict(lq=0),
+                                dict(b=0, q=None, k=None, v=None, o=None),
+                                dict(lq=0, q=None, o=None, lse=None)])
+def test_empty_work_is_a_noop(kw):
+    assert call(**kw) == 0
+
+
+def test_error_precedence_dtype_before_shape():
+    # a call with several faults reports the dtype one first
+    assert call(in_dt=3, hq=3, hkv=2) == 4
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(mi.MiAttnError) as e:
+        mi.mi_attn_fwd(q, q, q, q.clone())
+    assert e.value.status == 6
