@@ -26,6 +26,8 @@ struct FwdParams {
     float scale_log2;                // |scale| * log2(e), in fp32
     int32_t negate_q;                // 1 when scale < 0 (fold the sign into q)
     int32_t causal;
+    int32_t causal_pairs;            // causal q-tile order (0, 1 or 2)
+    int32_t key_split;               // waves per row group sharing its keys
 };
 
 // Storage tags for the element types (16-bit values are kept as raw bits).

@@ -17,6 +17,8 @@ namespace {
 
 thread_local int32_t g_last_hip_error = 0;
 
+constexpr int64_t kMaxRowStride = int64_t(1) << 24;   // elements
+
 bool aligned16(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
@@ -32,6 +34,30 @@ bool use_scalar_kernel() {
     static const bool v = [] {
         const char* e = std::getenv("MI_ATTN_KERNEL");
         return e != nullptr && std::strcmp(e, "simple") == 0;
+    }();
+    return v;
+}
+
+// Causal q-tile order of the MFMA kernel (MI_ATTN_CAUSAL_PAIRS): 0 = one
+// q-tile per work-group, heaviest first; 1 = q-tiles t and n-1-t in one
+// work-group; 2 (default) = one q-tile per work-group, first half of the grid
+// heaviest first and second half lightest first.
+int causal_pairs_setting() {
+    static const int v = [] {
+        const char* e = std::getenv("MI_ATTN_CAUSAL_PAIRS");
+        if (e == nullptr) return 2;
+        const int x = std::atoi(e);
+        return (x >= 0 && x <= 2) ? x : 2;
+    }();
+    return v;
+}
+
+// MI_ATTN_KEY_SPLIT=1|2: waves per 32-row group of the MFMA kernel (2 splits
+// the key tiles of a row group between two waves).
+int key_split_setting() {
+    static const int v = [] {
+        const char* e = std::getenv("MI_ATTN_KEY_SPLIT");
+        return (e != nullptr && std::strcmp(e, "1") == 0) ? 1 : 2;
     }();
     return v;
 }
@@ -87,6 +113,9 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
         o_strides ? *o_strides : default_strides(packed, hq, lq, head_dim);
     if (!stride_ok(qs) || !stride_ok(ks) || !stride_ok(vs) || !stride_ok(os))
         return MI_ATTN_ERR_LAYOUT;
+    // K/V tiles are fetched with 32-bit offsets from a tile's first row.
+    if (ks.row >= kMaxRowStride || vs.row >= kMaxRowStride)
+        return MI_ATTN_ERR_LAYOUT;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
         (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
         return MI_ATTN_ERR_LAYOUT;
@@ -115,6 +144,8 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
         std::fabs((double)scale) * 1.4426950408889634074, 1e-30);
     p.negate_q = scale < 0.0f ? 1 : 0;
     p.causal = causal;
+    p.causal_pairs = causal_pairs_setting();
+    p.key_split = key_split_setting();
 
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const hipError_t err =
