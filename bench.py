@@ -30,8 +30,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}   # MI355X dense MFMA, per GPU
-KERNEL_SRC = os.path.join(ROOT, "exact_attention_61_amd", "csrc",
-                          "attn_fwd_mfma.hip")
+# what the hot kernel is built from: its template, instantiations and flags
+KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_61_amd", *parts) for parts in
+               (("csrc", "attn_fwd_mfma.hpp"), ("csrc", "attn_fwd_mfma_d64.hip"),
+                ("csrc", "attn_fwd_mfma_d128.hip"), ("csrc", "common.hpp"),
+                ("build.py",))]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_mfma_traffic.json")
 
 
@@ -59,8 +62,11 @@ def algorithmic_bytes(w, inp):
 
 
 def kernel_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload):

@@ -33,6 +33,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-file code-generation options.  The d = 64 kernel keeps every MFMA
+# result in architectural VGPRs: its state fits in 256 of them, and results
+# in AGPRs would cost one copy instruction per score to reach the softmax.
+FILE_FLAGS = {
+    "attn_fwd_mfma_d64.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+}
+
+
 def _hipcc():
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"),
                  "/opt/rocm/bin/hipcc"):
@@ -56,7 +64,8 @@ def build(verbose=False, extra_flags=()):
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = max(1, min(len(srcs), os.cpu_count() or 1, 8))
-    cmds = [[hipcc, *HIPCC_FLAGS, *extra_flags, "-c", s, "-o", o]
+    cmds = [[hipcc, *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(s), ()),
+             *extra_flags, "-c", s, "-o", o]
             for s, o in zip(srcs, objs)]
     with cf.ThreadPoolExecutor(jobs) as ex:
         for cmd, _ in zip(cmds, ex.map(_run, cmds)):

@@ -1,0 +1,948 @@
+// MFMA attention forward for gfx950 (CDNA4): the library's hot path.
+//
+// Method.  Standard attention S = QK^T * scale, P = softmax(S), O = PV,
+// computed tile by tile so that S and P never leave the registers, with the
+// online-softmax statistics of "FlashAttention: turning the quadratic
+// intermediate matrices into statistics" (section 3.1): per query row a
+// reference max m, the exp-sum l relative to m and the output accumulator
+// relative to m; when m is replaced by a larger m', l and the accumulator are
+// multiplied by 2^(m - m').  Exponentials are base 2 with the scale and
+// log2(e) folded into one fp32 factor applied to the fp32 scores (inputs are
+// never pre-scaled in 16-bit), and l sums the fp32 probabilities.  Partial
+// results over disjoint key sets combine the same way (m = max of the two,
+// each side scaled by 2^(m_side - m)), which is how the waves that share a
+// row block merge their results at the end.
+//
+// The reference max is only replaced when a tile's max exceeds it by more
+// than a gap of 8 (log2 units), and the rescale is skipped when no row of the
+// wave needs it.  Any reference value gives the same O = u / l and LSE =
+// m + log2 l; probabilities stay below 2^8, far inside every range, and the
+// rescale of the accumulator is skipped on almost every tile.  The output is
+// normalised by the sum of the probabilities as rounded for the PV product
+// (one v_dot2 per pair), so that the rounding of a dominant probability
+// cancels between numerator and denominator.  The log-sum-exp uses that sum
+// for fp16 inputs (2^-11 relative at most) and an fp32 sum for bf16 inputs.
+//
+// Work decomposition.  A work-group of 4 waves owns BM = 128 query rows of
+// one (batch, head) at a time and walks the keys in tiles of BN = 64 keys.
+// Its waves form a 2 x 2 grid: wave w takes the 64 rows of row half w & 1
+// (two 32-row blocks) against the 32 keys of key half w >> 1 of every tile,
+// so each K and V fragment read from LDS feeds two products.  At the end the
+// two waves of a row half merge their partial results through LDS.  d = 64:
+// two work-groups per CU (256 registers per wave, 80 KiB of LDS each), so
+// that each SIMD runs waves of two independent work-groups whose softmax and
+// matrix products interleave; d = 128 (the accumulator alone takes 128
+// registers): one work-group per CU.
+//
+// K and V tiles go from global memory straight into LDS (buffer_load_dwordx4
+// ... lds) through a ring of 5 stages, 3 tiles ahead of use, with one
+// barrier per tile.  The stages are separate LDS arrays and the loop is
+// unrolled by 5, so the compiler can see that a fragment read never touches a
+// stage a copy is still landing in.
+//
+// Software pipeline.  Step j of a wave interleaves, in one instruction
+// stream, the matrix products of two neighbouring tiles with the vector work
+// of the tile between them: S(j+1) = Q K(j+1)^T and O += P(j-1) V(j-1) on the
+// matrix cores while the softmax of S(j) runs on the vector ALUs.
+//
+// LDS layout.  Tiles are stored fragment-major: every 1 KiB block holds
+// exactly the 64 lanes' operands of one MFMA (K) or of two transposing reads
+// (V), in lane order.  Every fragment read is then one contiguous,
+// bank-conflict-free access at a per-lane base plus an immediate offset, and
+// each DMA instruction fills one block.
+//
+// Transposed products.  A wave computes S^T = K Q^T and O^T = V^T P^T with
+// v_mfma_f32_32x32x16_{f16,bf16}.  In the 32x32 result layout lane l holds
+// column l % 32, i.e. one query row, so every lane owns all of its row's
+// scores (shared with lane l ^ 32): row maxima and sums are lane-local plus
+// one v_permlane32_swap, the rescale needs no data movement, and the S^T
+// accumulator already has the lane layout of the P^T operand of the second
+// product (the contraction order over keys is permuted the same way on both
+// operands).  V^T operands come from ds_read_b64_tr_b16, which transposes
+// 16-bit data within 16-lane groups.
+//
+// Causal masking is bottom-right aligned (key j visible to row i iff
+// j <= i + Lk - Lq): key tiles wholly above the diagonal of a q-tile are
+// never loaded, and the per-key mask is applied only on tiles that straddle
+// the diagonal or the key tail.  For causal inputs a work-group may process
+// q-tiles t and n-1-t one after the other, so that every work-group does the
+// same amount of work.
+//
+// This header holds the kernel template; attn_fwd_mfma_d64.hip and
+// attn_fwd_mfma_d128.hip instantiate it per head dimension, so that each can
+// be compiled with its own code-generation options.
+#pragma once
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace mi_attn {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kBM = 128;     // query rows per q-tile
+constexpr int kStages = 5;   // LDS ring of K/V tiles
+
+template <typename T> struct Mma;
+template <> struct Mma<f16_t> {
+    static constexpr float kGap = 8.0f;   // reference-max lag allowed (log2)
+    __device__ __forceinline__ static f32x16_t run(u32x4_t a, u32x4_t b,
+                                                   f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
+            0, 0, 0);
+    }
+    // The row sum is taken over the rounded P (v_dot2_f32_f16 with ones):
+    // fp16 rounding moves it by at most 2^-11 relative, i.e. the log-sum-exp
+    // by at most 4.9e-4, and the output normalisation matches the product.
+    static constexpr bool kFp32Sum = false;
+    __device__ __forceinline__ static float add_pair(uint32_t pr, float c) {
+        const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pr), one, c,
+                                      false);
+    }
+    // two fp32 -> packed 16-bit, round to nearest even (v_cvt_pk_f16_f32)
+    __device__ __forceinline__ static uint32_t pack(float x, float y) {
+        half2_t r;
+        r[0] = (_Float16)x;
+        r[1] = (_Float16)y;
+        return __builtin_bit_cast(uint32_t, r);
+    }
+};
+template <> struct Mma<bf16_t> {
+    static constexpr float kGap = 8.0f;
+    __device__ __forceinline__ static f32x16_t run(u32x4_t a, u32x4_t b,
+                                                   f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+            c, 0, 0, 0);
+    }
+    // bf16 rounding is too coarse for the log-sum-exp: it uses an fp32 sum,
+    // the output normalisation the sum of the rounded P.
+    static constexpr bool kFp32Sum = true;
+    // c + the two packed bf16 values (exact products with 1, fp32 sum)
+    __device__ __forceinline__ static float add_pair(uint32_t pr, float c) {
+        const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr),
+                                               one, c, false);
+    }
+    // v_cvt_pk_bf16_f32, round to nearest even
+    __device__ __forceinline__ static uint32_t pack(float x, float y) {
+        bf16x2_t r;
+        r[0] = (__bf16)x;
+        r[1] = (__bf16)y;
+        return __builtin_bit_cast(uint32_t, r);
+    }
+};
+
+// Value of x held by lane l ^ 32.
+__device__ __forceinline__ float partner(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t y = (threadIdx.x & 32) ? r[0] : r[1];
+    return __builtin_bit_cast(float, y);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+    return __builtin_amdgcn_exp2f(x);   // v_exp_f32; 2^-inf = 0
+}
+
+// IEEE maximum (v_maximum3_f32 when nested); no NaN canonicalisation.
+__device__ __forceinline__ float max2(float a, float b) {
+    return __builtin_elementwise_maximum(a, b);
+}
+
+// Pointers into LDS keep their address space through selects and phis.
+typedef __attribute__((address_space(3))) uint16_t lds16_t;
+typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f32x4_t lds_f4_t;
+typedef __attribute__((address_space(3))) float lds_f32_t;
+
+__device__ __forceinline__ s16x4_t lds_read_tr(const lds16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(p));
+}
+
+// s_waitcnt with vmcnt <= V and lgkmcnt == 0 (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8).
+template <int V>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(V >= 0 && V < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | ((V >> 4) << 14));
+}
+// s_waitcnt with vmcnt <= V only (expcnt and lgkmcnt at their maxima).
+template <int V>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(V >= 0 && V < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
+}
+
+// Empty asm that reads and redefines x: the value must be computed before
+// this point, so no optimisation sinks its computation into a later step.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(u32x4_t& x) { asm volatile("" : "+v"(x)); }
+
+template <typename Tout> struct Epi;
+template <> struct Epi<f16_t> {
+    __device__ __forceinline__ static void store4(void* o, int64_t i, float a,
+                                                  float b, float c, float d) {
+        u32x2_t v;
+        v[0] = Mma<f16_t>::pack(a, b);
+        v[1] = Mma<f16_t>::pack(c, d);
+        *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(o) + i) = v;
+    }
+};
+template <> struct Epi<bf16_t> {
+    __device__ __forceinline__ static void store4(void* o, int64_t i, float a,
+                                                  float b, float c, float d) {
+        u32x2_t v;
+        v[0] = Mma<bf16_t>::pack(a, b);
+        v[1] = Mma<bf16_t>::pack(c, d);
+        *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(o) + i) = v;
+    }
+};
+template <> struct Epi<float> {
+    __device__ __forceinline__ static void store4(void* o, int64_t i, float a,
+                                                  float b, float c, float d) {
+        float4 v = {a, b, c, d};
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(o) + i) = v;
+    }
+};
+
+// Fragment-major tile layout (16-bit elements; a stage holds K then V).
+//   K block kb*NKS + ks (512 elements): lane l's 8 elements are
+//     K[kb*32 + (l & 31)][(2*ks + (l >> 5))*8 .. +7].
+//   V half-block (db*NKC + kc)*2 + r (256 elements): lane l's 4 elements are
+//     V[kc*16 + 8*r + 4*(l >> 5) + ((l & 15) >> 2)][db*32 + 16*((l >> 4) & 1)
+//       + 4*(l & 3) .. +3],
+//   the address pattern of a ds_read_b64_tr_b16 that yields the V^T operand
+//   of keys kc*16 + 8*r + 4*hi + 0..3 and columns db*32 + (l & 31).
+template <int D>
+struct Layout {
+    static constexpr int WAVES = 4;          // waves per work-group
+    static constexpr int WG_PER_CU = D == 64 ? 2 : 1;   // resident work-groups
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int KQ = WAVES / 2;     // key groups of 32 keys
+    static constexpr int BN = 32 * KQ;       // keys per tile
+    static constexpr int NKC = BN / 16;      // 16-key chunks per tile
+    static constexpr int NKS = D / 16;       // k-steps of QK^T
+    static constexpr int NDB = D / 32;       // 32-column blocks of O^T
+    static constexpr int ELEMS = BN * D;     // per tile and tensor
+    static constexpr int BLOCKS = ELEMS / 512;   // 1 KiB DMA blocks per tensor
+    static constexpr int STAGE = 2 * ELEMS;  // K + V
+    static constexpr int DPW = 2 * BLOCKS / WAVES;   // DMA blocks per wave
+    // merge area: per wave its accumulators (ACC floats per lane), then the
+    // (m, l, lr) of both row blocks of every wave
+    static constexpr int ACC = 2 * NDB * 16;
+    static constexpr int SLOTS_PER_STAGE = (STAGE * 2) / (ACC * 64 * 4);
+    static_assert(SLOTS_PER_STAGE >= 1, "merge slot fits a stage");
+    static_assert(WAVES / SLOTS_PER_STAGE <= kStages - 1, "merge area");
+    static_assert(WAVES * 2 * 3 * 64 * 4 <= STAGE * 2, "merge statistics");
+    static_assert(kStages * STAGE * 2 * WG_PER_CU <= 160 * 1024, "LDS per CU");
+};
+
+template <int D>
+struct Stages {
+    lds16_t* s[kStages];
+};
+
+template <int D, typename Tin, typename Tout, bool CAUSAL>
+__device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
+                                             int h, int b, const Stages<D>& st) {
+    using L = Layout<D>;
+    constexpr int BN = L::BN, KQ = L::KQ;
+    constexpr int NKC = L::NKC, NKS = L::NKS, NDB = L::NDB;
+    constexpr int DPW = L::DPW;
+    constexpr int STAGES = kStages;
+    constexpr int AHEAD = STAGES - 2;    // copies run AHEAD tiles ahead
+    static_assert(2 * L::BLOCKS % L::WAVES == 0, "blocks per wave");
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar
+    const int kq = wave >> 1;            // key group of every tile
+    const int rh = wave & 1;             // row half of the q-tile
+    const int hi = lane >> 5;            // which half of the wave
+    const int col = lane & 31;           // the query row this lane owns
+
+    int q0 = 0, lq_b = p.lq, k0 = 0, lk_b = p.lk;
+    const bool packed = p.cu_q != nullptr;
+    if (packed) {
+        q0 = p.cu_q[b];
+        lq_b = p.cu_q[b + 1] - q0;
+        k0 = p.cu_k[b];
+        lk_b = p.cu_k[b + 1] - k0;
+    }
+    const int row0 = qtile * kBM;
+    if (row0 >= lq_b) return;            // uniform over the work-group
+    const int g = h / p.group;
+    const int diag = lk_b - lq_b;        // key j visible to row i iff j <= i + diag
+
+    const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) +
+                         (packed ? 0 : (int64_t)b * p.q_sb) +
+                         (int64_t)h * p.q_sh + (int64_t)(q0 + row0) * p.q_sr;
+    const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) +
+                         (packed ? 0 : (int64_t)b * p.k_sb) +
+                         (int64_t)g * p.k_sh + (int64_t)k0 * p.k_sr;
+    const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v) +
+                         (packed ? 0 : (int64_t)b * p.v_sb) +
+                         (int64_t)g * p.v_sh + (int64_t)k0 * p.v_sr;
+
+    // Key tiles this q-tile needs.
+    int kend = lk_b;
+    if (CAUSAL) kend = min(kend, row0 + kBM + diag);
+    const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+    // Q fragments (B operand of S^T = K Q^T) of the wave's two row blocks:
+    // lane holds row `col` of block rb, columns ks*16 + 8*hi .. +7.
+    const int wrow0 = row0 + 64 * rh;    // first row of this wave
+    int qrow[2];
+    bool row_ok[2];
+    int my_last_key[2];
+    u32x4_t qf[2][NKS];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        qrow[rb] = wrow0 + 32 * rb + col;   // sequence-local
+        row_ok[rb] = qrow[rb] < lq_b;
+        my_last_key[rb] =
+            CAUSAL ? min(lk_b - 1, qrow[rb] + diag) : lk_b - 1;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            u32x4_t x = {0u, 0u, 0u, 0u};
+            if (row_ok[rb])
+                x = *reinterpret_cast<const u32x4_t*>(
+                    qg + (int64_t)(qrow[rb] - row0) * p.q_sr + ks * 16 + 8 * hi);
+            if (p.negate_q) x ^= 0x80008000u;   // scale < 0: fold the sign into q
+            qf[rb][ks] = x;
+        }
+    }
+
+    // DMA plan of this lane: which block of a tile it fills and the byte
+    // offset, from the tile's first row, of the 16 bytes it copies.  Copies
+    // go through a buffer resource whose range ends with the sequence, so
+    // rows past the key range read as zeros (their scores are masked anyway).
+    uint32_t dma_voff[DPW];
+    int dma_dst[DPW];
+    const bool dma_is_v = wave * DPW >= L::BLOCKS;   // waves copy K or V
+    const int64_t dma_sr = dma_is_v ? p.v_sr : p.k_sr;
+    const uint16_t* dma_base = dma_is_v ? vg : kg;
+#pragma unroll
+    for (int t = 0; t < DPW; ++t) {
+        const int blk = wave * DPW + t;   // 0 .. 2*BLOCKS-1
+        const int bi = dma_is_v ? blk - L::BLOCKS : blk;
+        int r, c;
+        if (!dma_is_v) {                 // K block bi = kb*NKS + ks
+            const int kb = bi / NKS, ks = bi % NKS;
+            r = kb * 32 + (lane & 31);
+            c = (2 * ks + (lane >> 5)) * 8;
+        } else {                         // V half-blocks 2*bi, 2*bi + 1
+            const int db = bi / NKC, kc = bi % NKC;
+            const int rr = lane >> 5;    // which half-block
+            const int t2 = 2 * (lane & 31);   // transposing-read lane covered
+            r = kc * 16 + 8 * rr + 4 * (t2 >> 5) + ((t2 & 15) >> 2);
+            c = db * 32 + 16 * ((t2 >> 4) & 1) + 4 * (t2 & 3);
+        }
+        dma_voff[t] = (uint32_t)(((int64_t)r * dma_sr + c) * 2);
+        dma_dst[t] = (dma_is_v ? L::ELEMS : 0) + bi * 512;
+    }
+    // Tiles past the last one get an empty range: their copies read nothing
+    // and write zeros, so every step issues the same copies and waits for
+    // the same counts.
+    auto tile_rsrc = [&](int kt) {
+        const int rows = kt < n_kt ? min(lk_b - kt * BN, BN) : 0;
+        const int bytes = __builtin_amdgcn_readfirstlane((int)(rows * dma_sr * 2));
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(dma_base + (int64_t)kt * BN * dma_sr), (short)0, bytes,
+            0x00020000);
+    };
+    auto issue_part = [&](auto rsrc, lds16_t* stage, int t) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void*)(stage + dma_dst[t]), 16,
+            dma_voff[t], 0, 0, 0);
+    };
+    auto issue_tile = [&](int kt, lds16_t* stage) {
+        const auto rsrc = tile_rsrc(kt);
+#pragma unroll
+        for (int t = 0; t < DPW; ++t) issue_part(rsrc, stage, t);
+    };
+
+    const float c2 = p.scale_log2;       // |scale| * log2(e)
+    float m[2], l[2], lr[2];             // per row block: reference max (log2
+    f32x16_t acc[2][NDB];                // domain), this lane's exp-sums, O^T
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        m[rb] = -__builtin_inff();
+        l[rb] = 0.0f;
+        lr[rb] = 0.0f;                   // sum of the rounded P
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x16_t{};
+    }
+
+    // Pipeline registers: S(j) of both row blocks, P(j-1) and the V(j-1)
+    // fragments of the wave's key group (16-key chunks c = 0, 1).  V(j-1) is
+    // read in the step that uses it; the products S(j+1) of row block 0 go
+    // first while it lands.
+    f32x16_t s_cur[2];
+    u32x4_t p_prev[2][2];
+    u32x4_t vf[NDB][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) p_prev[rb][c] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) vf[db][c] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+
+    // Per-lane element offsets of the wave's fragments in a stage, opaque to
+    // the optimiser: every fragment address is then one stage array plus one
+    // variable index plus a constant, a form whose stage the compiler can
+    // still tell apart from the stages copies are landing in.
+    int k_off = (kq * NKS) * 512 + lane * 8;
+    int v_off = L::ELEMS + (2 * kq) * 512 + lane * 4;
+    asm volatile("" : "+v"(k_off));
+    asm volatile("" : "+v"(v_off));
+    auto read_k = [&](const lds16_t* stage, u32x4_t (&kf)[NKS]) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            kf[ks] = *reinterpret_cast<lds_u32x4_t*>(stage + k_off + ks * 512);
+    };
+    auto read_v = [&](const lds16_t* stage) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const lds16_t* vb = stage + v_off + (db * NKC + c) * 512;
+                const u32x2_t a = __builtin_bit_cast(u32x2_t, lds_read_tr(vb));
+                const u32x2_t d = __builtin_bit_cast(u32x2_t, lds_read_tr(vb + 256));
+                vf[db][c] = u32x4_t{a[0], a[1], d[0], d[1]};
+            }
+    };
+    // -inf for the scores of keys past the row's last visible key; applied
+    // only in steps whose tile may hold such keys for some row of the
+    // work-group (causal diagonal, end of the key range).
+    auto mask_cur = [&](int kt) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int lim = my_last_key[rb] - (kt * BN + 32 * kq + 4 * hi);
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (8 * (e >> 2) + (e & 3) > lim) s_cur[rb][e] = -__builtin_inff();
+        }
+    };
+    auto pv_last = [&]() {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+                    acc[rb][db] = Mma<Tin>::run(vf[db][c], p_prev[rb][c], acc[rb][db]);
+    };
+
+    // Softmax of S(j) in its full form: row max (with lane ^ 32), reference
+    // update when the tile's max exceeds the reference by more than the gap,
+    // p = 2^(s*c2 - m), rounded P and row sums, rescale of l, lr and the
+    // accumulators (after the previous tile's product).  Used for a q-tile's
+    // first tile and whenever the short form below may have left range.
+    auto softmax_full = [&](u32x4_t (&p_new)[2][2]) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const f32x16_t& x = s_cur[rb];
+            const float a0 = max2(max2(x[0], x[1]), x[2]);
+            const float a1 = max2(max2(x[3], x[4]), x[5]);
+            const float a2 = max2(max2(x[6], x[7]), x[8]);
+            const float a3 = max2(max2(x[9], x[10]), x[11]);
+            const float a4 = max2(max2(x[12], x[13]), x[14]);
+            const float mx = max2(max2(max2(a0, a1), a2), max2(max2(a3, a4), x[15]));
+            const float mt = max2(mx, partner(mx)) * c2;
+            const bool grow = mt > m[rb] + Mma<Tin>::kGap;   // false if all -inf
+            const float m_new = grow ? mt : m[rb];
+            const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
+            float rs = 0.0f, rsr = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                s_cur[rb][e] = fast_exp2(fmaf(s_cur[rb][e], c2, -m_use));
+                rs += s_cur[rb][e];
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int e = 8 * c + 2 * jj;
+                    p_new[rb][c][jj] = Mma<Tin>::pack(s_cur[rb][e], s_cur[rb][e + 1]);
+                    rsr = Mma<Tin>::add_pair(p_new[rb][c][jj], rsr);
+                }
+            const float alpha = grow ? fast_exp2(m[rb] - m_new) : 1.0f;
+            l[rb] = l[rb] * alpha + (Mma<Tin>::kFp32Sum ? rs : 0.0f);
+            lr[rb] = lr[rb] * alpha + rsr;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[rb][db] *= alpha;
+            m[rb] = m_new;
+        }
+    };
+
+    // One pipeline step for tile j.  The matrix products of the step -- with
+    // NEXT S(j+1) = Q K(j+1)^T of row block 0, then (with PV) O += P(j-1)
+    // V(j-1), then S(j+1) of row block 1 -- are spread between groups of the
+    // vector work of the softmax of S(j), which depends on none of them.
+    // Scheduling barriers keep the order, so the wave issues a product and
+    // then vector work while the matrix core runs it.
+    //
+    // Reference update: every lane takes the max of its own 16 scores of a
+    // row; only when some lane's max exceeds its row's reference by more than
+    // the gap (rarely, after a row's first tile) does the wave exchange the
+    // maxima with lane ^ 32, move the references of the rows whose tile max
+    // exceeds them by more than the gap, and rescale.  FULL (first tile of a
+    // q-tile): the full form, with every row's reference set from the tile.
+    auto compute = [&](int j, auto NEXT, auto PV, auto MASK, auto FULL,
+                       const u32x4_t (&kf)[NKS], f32x16_t (&s_next)[2],
+                       int dma_kt, lds16_t* dma_stage) {
+        constexpr bool next = decltype(NEXT)::value;
+        constexpr int NPV = decltype(PV)::value ? 2 * NDB * 2 : 0;
+        constexpr int NQK = next ? 2 * NKS : 0;
+        constexpr int NM = NPV + NQK;
+        constexpr int PV0 = NQK / 2;     // first PV product
+        constexpr int kGroups = 13;
+        auto mfma = [&](int q) {
+            if (q >= PV0 && q < PV0 + NPV) {
+                const int qp = q - PV0;
+                const int c = qp / (2 * NDB), r2 = qp % (2 * NDB);
+                const int db = r2 / 2, rb2 = r2 % 2;
+                acc[rb2][db] = Mma<Tin>::run(vf[db][c], p_prev[rb2][c], acc[rb2][db]);
+            } else if (next) {
+                const int qq = q < PV0 ? q : q - NPV;
+                const int rb2 = qq / NKS, ks = qq % NKS;
+                s_next[rb2] = Mma<Tin>::run(kf[ks], qf[rb2][ks],
+                                            ks == 0 ? f32x16_t{} : s_next[rb2]);
+            }
+        };
+        if constexpr (decltype(MASK)::value) mask_cur(j);
+        u32x4_t p_new[2][2];             // this tile's P; p_prev stays for PV
+        if constexpr (decltype(FULL)::value) {
+            if (next) issue_tile(dma_kt, dma_stage);
+#pragma unroll
+            for (int q = 0; q < NM; ++q) mfma(q);
+            softmax_full(p_new);
+        } else {
+            // The copy of tile dma_kt (NEXT only), one instruction every few
+            // groups: a burst of copies from every wave at once fills the
+            // memory pipeline's queue and stalls the waves behind it.
+            const auto rsrc = tile_rsrc(dma_kt);
+            float psum[2][4];
+            float rsr[2][2];             // row sums of the rounded P, per chunk
+            float m_use[2];
+            bool upd;                    // some reference moved (wave-uniform)
+            float alpha[2] = {1.0f, 1.0f};
+#pragma unroll
+            for (int gi = 0; gi < kGroups; ++gi) {
+                if (gi == 0) {
+                    // lane maxima of both row blocks; rare reference update
+                    float mt[2];
+                    bool need[2];
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb) {
+                        const f32x16_t& x = s_cur[rb];
+                        const float a0 = max2(max2(x[0], x[1]), x[2]);
+                        const float a1 = max2(max2(x[3], x[4]), x[5]);
+                        const float a2 = max2(max2(x[6], x[7]), x[8]);
+                        const float a3 = max2(max2(x[9], x[10]), x[11]);
+                        const float a4 = max2(max2(x[12], x[13]), x[14]);
+                        mt[rb] = max2(max2(max2(a0, a1), a2),
+                                      max2(max2(a3, a4), x[15])) * c2;
+                        need[rb] = mt[rb] > m[rb] + Mma<Tin>::kGap;
+                    }
+                    upd = __builtin_amdgcn_ballot_w64(need[0] || need[1]) != 0;
+                    if (upd) {
+                        asm volatile("");   // keep this a branch: rarely taken
+#pragma unroll
+                        for (int rb = 0; rb < 2; ++rb) {
+                            const float mr = max2(mt[rb], partner(mt[rb]));
+                            const bool grow = mr > m[rb] + Mma<Tin>::kGap;
+                            const float m_new = grow ? mr : m[rb];
+                            alpha[rb] = grow ? fast_exp2(m[rb] - m_new) : 1.0f;
+                            l[rb] *= alpha[rb];
+                            lr[rb] *= alpha[rb];
+                            m[rb] = m_new;
+                        }
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb)
+                        m_use[rb] = m[rb] == -__builtin_inff() ? 0.0f : m[rb];
+                } else if (gi < 9) {
+                    // p = 2^(s*c2 - m) for 4 scores of row block gi & 1
+                    const int rb = (gi - 1) & 1, e0 = 4 * ((gi - 1) >> 1);
+                    float pe[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pe[i] = fast_exp2(fmaf(s_cur[rb][e0 + i], c2, -m_use[rb]));
+                        pin(pe[i]);   // computed in this group, not sunk
+                        s_cur[rb][e0 + i] = pe[i];
+                    }
+                    if (Mma<Tin>::kFp32Sum) {
+                        psum[rb][(gi - 1) >> 1] = (pe[0] + pe[1]) + (pe[2] + pe[3]);
+                        pin(psum[rb][(gi - 1) >> 1]);
+                    }
+                } else {
+                    // P^T operand of 16-key chunk c of row block rb: elements
+                    // 8c .. 8c+7 of s_cur[rb], rounded to the input type
+                    const int rb = (gi - 9) >> 1, c = (gi - 9) & 1;
+                    float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int e = 8 * c + 2 * jj;
+                        p_new[rb][c][jj] = Mma<Tin>::pack(s_cur[rb][e], s_cur[rb][e + 1]);
+                        if (jj & 1) t1 = Mma<Tin>::add_pair(p_new[rb][c][jj], t1);
+                        else t0 = Mma<Tin>::add_pair(p_new[rb][c][jj], t0);
+                    }
+                    rsr[rb][c] = t0 + t1;
+                    pin(p_new[rb][c]);
+                    pin(rsr[rb][c]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q = gi * NM / kGroups; q < (gi + 1) * NM / kGroups; ++q)
+                    mfma(q);
+                if (next) {
+#pragma unroll
+                    for (int t = 0; t < DPW; ++t)
+                        if (gi == 1 + t * (kGroups - 1) / DPW) issue_part(rsrc, dma_stage, t);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                if (Mma<Tin>::kFp32Sum)
+                    l[rb] += (psum[rb][0] + psum[rb][1]) + (psum[rb][2] + psum[rb][3]);
+                lr[rb] += rsr[rb][0] + rsr[rb][1];
+            }
+            // the accumulators hold P(j-1) V(j-1), relative to the old
+            // references, only once this step's products are in
+            if (upd) {
+                asm volatile("");   // keep this a branch: rarely taken
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) acc[rb][db] *= alpha[rb];
+            }
+        }
+        // the step's results are produced here, not where they are used
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                pin(p_new[rb][c]);
+                p_prev[rb][c] = p_new[rb][c];
+            }
+    };
+
+    // Stage of tile t, picked without a runtime index into the ring.
+    auto stage_of = [&](int t) {
+        const int sl = t % STAGES;
+        lds16_t* x = st.s[0];
+        if (sl == 1) x = st.s[1];
+        if (sl == 2) x = st.s[2];
+        if (sl == 3) x = st.s[3];
+        if (sl == 4) x = st.s[4];
+        return x;
+    };
+
+    // Key tiles 0 .. n_full-1 need no mask for any row of the work-group:
+    // they end inside the key range and, for causal inputs, at or before the
+    // last key visible to the first row.
+    int n_full = lk_b / BN;
+    if (CAUSAL) {
+        const int lim = row0 + diag + 1;
+        n_full = min(n_full, lim > 0 ? lim / BN : 0);
+    }
+
+    // Step j (0 <= j <= n_kt - 2): tile t lives in stage t % STAGES.  K of
+    // tile j+1 and V of tile j-1 are read here.  The stage refilled here,
+    // (j + AHEAD) % STAGES = (j-2) % STAGES, was last read (V of tile j-2)
+    // one step ago, and those fragments were consumed by products of that
+    // step, so every wave is done with it once it reaches this step's
+    // barrier.
+    //   steady: stage S = j % STAGES known at compile time, no mask; FIRST
+    //           (j == 0) has no P(j-1) V(j-1).
+    //   masked: any j >= n_full, stages picked at run time.
+    auto steady = [&](int j, auto SI, auto FIRST) {
+        constexpr int S = decltype(SI)::value;
+        constexpr bool first = decltype(FIRST)::value;
+        // tile j+1 has landed once at most the copies issued after it
+        // (tiles j+2 .. j+AHEAD-1) are pending
+        wait_vm<(AHEAD - 2) * DPW>();
+        __builtin_amdgcn_s_barrier();
+        u32x4_t kf[NKS];
+        read_k(st.s[(S + 1) % STAGES], kf);
+        if constexpr (!first) read_v(st.s[(S + STAGES - 1) % STAGES]);
+        f32x16_t s_new[2];
+        compute(j, std::true_type(), std::integral_constant<bool, !first>(),
+                std::false_type(), std::integral_constant<bool, first>(), kf,
+                s_new, j + AHEAD, st.s[(S + AHEAD) % STAGES]);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) s_cur[rb] = s_new[rb];
+    };
+    auto masked = [&](int j) {
+        wait_vm<(AHEAD - 2) * DPW>();
+        __builtin_amdgcn_s_barrier();
+        u32x4_t kf[NKS];
+        read_k(stage_of(j + 1), kf);
+        if (j > 0) read_v(stage_of(j - 1));   // else P(j-1) = 0 and V = 0
+        f32x16_t s_new[2];
+        compute(j, std::true_type(), std::true_type(), std::true_type(),
+                std::false_type(), kf, s_new, j + AHEAD, stage_of(j + AHEAD));
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) s_cur[rb] = s_new[rb];
+    };
+
+    if (n_kt > 0) {
+        // prologue: tiles 0 .. AHEAD-1 in flight; wait for tile 0 and
+        // compute S(0)
+#pragma unroll
+        for (int t = 0; t < AHEAD; ++t) issue_tile(t, st.s[t]);
+        wait_vm<(AHEAD - 1) * DPW>();    // tiles 1 .. AHEAD-1 may be pending
+        __builtin_amdgcn_s_barrier();
+        {
+            u32x4_t kf[NKS];
+            read_k(st.s[0], kf);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                s_cur[rb] = f32x16_t{};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    s_cur[rb] = Mma<Tin>::run(kf[ks], qf[rb][ks], s_cur[rb]);
+            }
+        }
+        static_assert(STAGES == 5, "unrolling below");
+        // unmasked steps 0 .. n_un-1: step 0, then rounds of STAGES steps
+        // starting at stage 1, then the remainder
+        const int n_un = min(n_full, n_kt - 1);
+        int j = 0;
+        if (n_un >= 1) steady(j++, I0(), std::true_type());
+        for (; j + STAGES <= n_un; j += STAGES) {
+            steady(j, I1(), std::false_type());
+            steady(j + 1, I2(), std::false_type());
+            steady(j + 2, I3(), std::false_type());
+            steady(j + 3, I4(), std::false_type());
+            steady(j + 4, I0(), std::false_type());
+        }
+        // remaining unmasked steps (j < n_un), j % STAGES == 1 here
+        if (j < n_un) {
+            steady(j++, I1(), std::false_type());
+            if (j < n_un) {
+                steady(j++, I2(), std::false_type());
+                if (j < n_un) {
+                    steady(j++, I3(), std::false_type());
+                    if (j < n_un) steady(j++, I4(), std::false_type());
+                }
+            }
+        }
+        // masked steps up to n_kt - 2
+        for (; j <= n_kt - 2; ++j) masked(j);
+        // last tile jl: no copy in flight, no product S(jl+1); then its own PV
+        {
+            const int jl = n_kt - 1;
+            wait_vm_lgkm0<0>();
+            u32x4_t kf_unused[NKS];
+            f32x16_t s_unused[2];
+            if (jl > 0) read_v(stage_of(jl - 1));
+            if (jl >= n_full)
+                compute(jl, std::false_type(), std::true_type(), std::true_type(),
+                        std::false_type(), kf_unused, s_unused, 0, st.s[0]);
+            else
+                compute(jl, std::false_type(), std::true_type(), std::false_type(),
+                        std::false_type(), kf_unused, s_unused, 0, st.s[0]);
+            read_v(stage_of(jl));
+            pv_last();
+        }
+    }
+
+    // Merge of the KQ waves that share a row half.  Every wave stores its
+    // (m, l, lr) and accumulators, relative to its own reference max, in
+    // LDS; then each of them finishes 2*NDB/KQ of the half's 2*NDB output
+    // blocks (row block rb, 32-column block db):
+    //   m = max_q m_q,  x = sum_q x_q 2^(m_q - m).
+    constexpr int SPS = L::SLOTS_PER_STAGE;
+    constexpr int BPW = 2 * NDB / KQ;    // output blocks per wave
+    __syncthreads();                     // every wave is done with the ring
+    auto slot_acc = [&](int w) {
+        lds16_t* base = st.s[0];
+        const int si = w / SPS;
+        if (si == 1) base = st.s[1];
+        if (si == 2) base = st.s[2];
+        if (si == 3) base = st.s[3];
+        return reinterpret_cast<lds_f4_t*>(base) + (w % SPS) * (L::ACC / 4) * 64;
+    };
+    auto stat = [&](int w, int rb, int k) {
+        return reinterpret_cast<lds_f32_t*>(st.s[STAGES - 1]) +
+               ((w * 2 + rb) * 3 + k) * 64;
+    };
+    {
+        lds_f4_t* a = slot_acc(wave);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg)
+                    a[((rb * NDB + db) * 4 + gg) * 64 + lane] =
+                        f32x4_t{acc[rb][db][4 * gg], acc[rb][db][4 * gg + 1],
+                                acc[rb][db][4 * gg + 2], acc[rb][db][4 * gg + 3]};
+            stat(wave, rb, 0)[lane] = m[rb];
+            stat(wave, rb, 1)[lane] = l[rb];
+            stat(wave, rb, 2)[lane] = lr[rb];
+        }
+    }
+    __syncthreads();
+
+    auto finish = [&](const int bi) {
+        const int rb = bi / NDB, db = bi % NDB;
+        float mq[KQ];
+        float mt = -__builtin_inff();
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+            mq[q] = stat(rh + 2 * q, rb, 0)[lane];
+            mt = max2(mt, mq[q]);
+        }
+        const float mu = mt == -__builtin_inff() ? 0.0f : mt;
+        float lf = 0.0f, lrf = 0.0f;
+        f32x16_t o = f32x16_t{};
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+            const int w = rh + 2 * q;
+            const float f = fast_exp2(mq[q] - mu);
+            lf += stat(w, rb, 1)[lane] * f;
+            lrf += stat(w, rb, 2)[lane] * f;
+            const lds_f4_t* a = slot_acc(w) + ((rb * NDB + db) * 4) * 64 + lane;
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                const f32x4_t x = a[gg * 64];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[4 * gg + i] += x[i] * f;
+            }
+        }
+        // O is normalised by the sum of the rounded P, LSE uses the fp32 sum
+        // where there is one.
+        const float ln = lrf + partner(lrf);
+        const float lt = Mma<Tin>::kFp32Sum ? lf + partner(lf) : ln;
+        if (row_ok[rb]) {
+            const float inv = ln > 0.0f ? 1.0f / ln : 0.0f;
+            const int64_t orow = (packed ? 0 : (int64_t)b * p.o_sb) +
+                                 (int64_t)h * p.o_sh +
+                                 (int64_t)(q0 + qrow[rb]) * p.o_sr;
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                const int d0 = db * 32 + 8 * gg + 4 * hi;
+                Epi<Tout>::store4(p.o, orow + d0, o[4 * gg] * inv,
+                                  o[4 * gg + 1] * inv, o[4 * gg + 2] * inv,
+                                  o[4 * gg + 3] * inv);
+            }
+            if (db == 0 && p.lse != nullptr && hi == 0) {
+                const float lse = lt > 0.0f
+                                      ? (mu + __log2f(lt)) * 0.69314718055994530942f
+                                      : -__builtin_inff();
+                const int64_t li =
+                    packed ? (int64_t)h * p.cu_q[p.batch] + q0 + qrow[rb]
+                           : ((int64_t)b * p.hq + h) * p.lq + qrow[rb];
+                p.lse[li] = lse;
+            }
+        }
+    };
+    // output blocks bi = kq*BPW .. kq*BPW + BPW - 1
+#pragma unroll
+    for (int bi = 0; bi < 2 * NDB; ++bi)
+        if (bi / BPW == kq) finish(bi);
+}
+
+// Grid: blockIdx.x = item * (hq * batch) + (batch, head) index, so that
+// consecutive work-groups take the same item of different heads.  Items are
+// q-tiles, heaviest first for causal inputs.  With `pair` (causal only) item t
+// covers q-tiles n-1-t and t, which together see n+1 key tiles; the middle
+// tile of an odd count runs alone.
+template <int D, typename Tin, typename Tout, bool CAUSAL>
+__global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn_fwd_mfma_kernel(
+    FwdParams p, int n_qtiles, int pair) {
+    __shared__ __attribute__((aligned(16))) uint16_t st0[Layout<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t st1[Layout<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t st2[Layout<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t st3[Layout<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t st4[Layout<D>::STAGE];
+    Stages<D> st;
+    st.s[0] = (lds16_t*)st0;
+    st.s[1] = (lds16_t*)st1;
+    st.s[2] = (lds16_t*)st2;
+    st.s[3] = (lds16_t*)st3;
+    st.s[4] = (lds16_t*)st4;
+    const int bh_count = p.hq * p.batch;
+    const int item = (int)blockIdx.x / bh_count;
+    const int bh = (int)blockIdx.x - item * bh_count;
+    const int h = bh % p.hq;
+    const int b = bh / p.hq;
+    // q-tiles of this work-group (one call site keeps the code compact)
+    int tiles[2] = {item, -1};
+    if (CAUSAL) {
+        if (pair == 2) {
+            // first half of the grid heaviest-first, second half
+            // lightest-first: work-groups i and i + grid/2, which the
+            // dispatcher tends to place on the same CU, see n+1 key tiles
+            const int half = n_qtiles / 2;
+            tiles[0] = item < half ? n_qtiles - 1 - item : item - half;
+        } else {
+            tiles[0] = n_qtiles - 1 - item;
+            if (pair == 1 && item < tiles[0]) tiles[1] = item;
+        }
+    }
+    for (int it = 0; it < 2 && tiles[it] >= 0; ++it) {
+        if (it > 0) __syncthreads();     // the LDS stages are reused
+        attend_qtile<D, Tin, Tout, CAUSAL>(p, tiles[it], h, b, st);
+    }
+}
+
+template <int D, typename Tin, typename Tout>
+hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
+    const int n_qtiles = (p.lq + kBM - 1) / kBM;
+    // causal q-tile order: with two resident work-groups per CU, grid halves
+    // heaviest-first and lightest-first; with one, q-tile pairs
+    const int pair = !p.causal ? 0
+                     : p.causal_pairs >= 0 ? p.causal_pairs
+                     : (Layout<D>::WG_PER_CU == 2 ? 2 : 1);
+    const int items = pair == 1 ? (n_qtiles + 1) / 2 : n_qtiles;
+    const int64_t blocks = (int64_t)items * p.hq * p.batch;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (p.causal)
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true>),
+                           dim3((unsigned)blocks), dim3(Layout<D>::THREADS), 0,
+                           stream, p, n_qtiles, pair);
+    else
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, false>),
+                           dim3((unsigned)blocks), dim3(Layout<D>::THREADS), 0,
+                           stream, p, n_qtiles, 0);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdParams& p, int in_dtype, int out_dtype,
+                    hipStream_t stream) {
+    if (in_dtype == 0) {
+        return out_dtype == 2 ? launch_typed<D, f16_t, float>(p, stream)
+                              : launch_typed<D, f16_t, f16_t>(p, stream);
+    }
+    return out_dtype == 2 ? launch_typed<D, bf16_t, float>(p, stream)
+                          : launch_typed<D, bf16_t, bf16_t>(p, stream);
+}
+
+}  // namespace
+}  // namespace mi_attn

@@ -1,0 +1,11 @@
+// Instantiation of the MFMA attention forward kernel for head dimension 128.
+#include "attn_fwd_mfma.hpp"
+
+namespace mi_attn {
+
+hipError_t launch_mfma_d128(const FwdParams& p, int in_dtype, int out_dtype,
+                          hipStream_t stream) {
+    return launch_d<128>(p, in_dtype, out_dtype, stream);
+}
+
+}  // namespace mi_attn

@@ -26,8 +26,7 @@ struct FwdParams {
     float scale_log2;                // |scale| * log2(e), in fp32
     int32_t negate_q;                // 1 when scale < 0 (fold the sign into q)
     int32_t causal;
-    int32_t causal_pairs;            // causal q-tile order (0, 1 or 2)
-    int32_t key_split;               // waves per row group sharing its keys
+    int32_t causal_pairs;            // causal q-tile order (0, 1, 2; -1 default)
 };
 
 // Storage tags for the element types (16-bit values are kept as raw bits).
@@ -76,7 +75,9 @@ template <> struct OutStore<float> {
 // argument was validated by the caller.  Return the hipGetLastError() code.
 hipError_t launch_simple(const FwdParams& p, int in_dtype, int out_dtype,
                          int head_dim, hipStream_t stream);
-hipError_t launch_mfma(const FwdParams& p, int in_dtype, int out_dtype,
-                       int head_dim, hipStream_t stream);
+hipError_t launch_mfma_d64(const FwdParams& p, int in_dtype, int out_dtype,
+                          hipStream_t stream);
+hipError_t launch_mfma_d128(const FwdParams& p, int in_dtype, int out_dtype,
+                           hipStream_t stream);
 
 }  // namespace mi_attn

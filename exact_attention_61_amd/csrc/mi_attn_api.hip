@@ -40,24 +40,15 @@ bool use_scalar_kernel() {
 
 // Causal q-tile order of the MFMA kernel (MI_ATTN_CAUSAL_PAIRS): 0 = one
 // q-tile per work-group, heaviest first; 1 = q-tiles t and n-1-t in one
-// work-group; 2 (default) = one q-tile per work-group, first half of the grid
-// heaviest first and second half lightest first.
+// work-group; 2 = one q-tile per work-group, first half of the grid heaviest
+// first and second half lightest first; unset (-1) = the kernel's default
+// for the head dimension.
 int causal_pairs_setting() {
     static const int v = [] {
         const char* e = std::getenv("MI_ATTN_CAUSAL_PAIRS");
-        if (e == nullptr) return 2;
+        if (e == nullptr) return -1;
         const int x = std::atoi(e);
-        return (x >= 0 && x <= 2) ? x : 2;
-    }();
-    return v;
-}
-
-// MI_ATTN_KEY_SPLIT=1|2: waves per 32-row group of the MFMA kernel (2 splits
-// the key tiles of a row group between two waves).
-int key_split_setting() {
-    static const int v = [] {
-        const char* e = std::getenv("MI_ATTN_KEY_SPLIT");
-        return (e != nullptr && std::strcmp(e, "1") == 0) ? 1 : 2;
+        return (x >= 0 && x <= 2) ? x : -1;
     }();
     return v;
 }
@@ -145,15 +136,16 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
     p.negate_q = scale < 0.0f ? 1 : 0;
     p.causal = causal;
     p.causal_pairs = causal_pairs_setting();
-    p.key_split = key_split_setting();
 
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const hipError_t err =
         use_scalar_kernel()
             ? mi_attn::launch_simple(p, (int)in_dtype, (int)out_dtype,
                                      head_dim, st)
-            : mi_attn::launch_mfma(p, (int)in_dtype, (int)out_dtype, head_dim,
-                                   st);
+            : head_dim == 64
+                  ? mi_attn::launch_mfma_d64(p, (int)in_dtype, (int)out_dtype, st)
+                  : mi_attn::launch_mfma_d128(p, (int)in_dtype, (int)out_dtype,
+                                              st);
     if (err != hipSuccess) {
         g_last_hip_error = (int32_t)err;
         return MI_ATTN_ERR_HIP;
