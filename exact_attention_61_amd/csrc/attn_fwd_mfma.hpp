@@ -72,6 +72,7 @@
 // attn_fwd_mfma_d128.hip instantiate it per head dimension, so that each can
 // be compiled with its own code-generation options.
 #pragma once
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -250,14 +251,18 @@ struct Layout {
     static_assert(kStages * STAGE * 2 * WG_PER_CU <= 160 * 1024, "LDS per CU");
 };
 
-template <int D>
-struct Stages {
-    lds16_t* s[kStages];
-};
+// Stage K of the LDS ring of a work-group (one array per stage, so that the
+// compiler tells a stage being read apart from one a copy is landing in).
+template <int D, int K>
+__device__ __forceinline__ lds16_t* ring() {
+    __shared__ __attribute__((aligned(16))) uint16_t r[Layout<D>::STAGE];
+    return (lds16_t*)r;
+}
 
 template <int D, typename Tin, typename Tout, bool CAUSAL>
 __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
-                                             int h, int b, const Stages<D>& st) {
+                                             int h, int b, int chunk,
+                                             int nchunks, int n_qtiles) {
     using L = Layout<D>;
     constexpr int BN = L::BN, KQ = L::KQ;
     constexpr int NKC = L::NKC, NKS = L::NKS, NDB = L::NDB;
@@ -302,34 +307,39 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                          (packed ? 0 : (int64_t)b * p.v_sb) +
                          (int64_t)g * p.v_sh + (int64_t)k0 * p.v_sr;
 
-    // Key tiles this q-tile needs.
+    // Key tiles this q-tile needs, and the chunk [kt0, kt1) of them this
+    // work-group takes (all of them unless the q-tile is split).
     int kend = lk_b;
     if (CAUSAL) kend = min(kend, row0 + kBM + diag);
-    const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
+    const int n_kt_all = kend > 0 ? (kend + BN - 1) / BN : 0;
+    const int kt0 = chunk * n_kt_all / nchunks;
+    const int kt1 = (chunk + 1) * n_kt_all / nchunks;
+    const int n_kt = kt1 - kt0;          // steps of this work-group
 
     // Q fragments (B operand of S^T = K Q^T) of the wave's two row blocks:
     // lane holds row `col` of block rb, columns ks*16 + 8*hi .. +7.
     const int wrow0 = row0 + 64 * rh;    // first row of this wave
-    int qrow[2];
-    bool row_ok[2];
-    int my_last_key[2];
+    // This lane's row of block rb (sequence-local) and the last key it may
+    // see; recomputed where needed rather than held across the key loop.
+    auto qrow = [&](int rb) { return wrow0 + 32 * rb + (int)(threadIdx.x & 31); };
+    auto last_key = [&](int rb) {
+        return CAUSAL ? min(lk_b - 1, qrow(rb) + diag) : lk_b - 1;
+    };
     u32x4_t qf[2][NKS];
+    // issued in the prologue between the copies of tiles 0 and 1, so that
+    // their latency overlaps the copies' and one wait covers both
+    auto load_q = [&]() {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        qrow[rb] = wrow0 + 32 * rb + col;   // sequence-local
-        row_ok[rb] = qrow[rb] < lq_b;
-        my_last_key[rb] =
-            CAUSAL ? min(lk_b - 1, qrow[rb] + diag) : lk_b - 1;
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            u32x4_t x = {0u, 0u, 0u, 0u};
-            if (row_ok[rb])
-                x = *reinterpret_cast<const u32x4_t*>(
-                    qg + (int64_t)(qrow[rb] - row0) * p.q_sr + ks * 16 + 8 * hi);
-            if (p.negate_q) x ^= 0x80008000u;   // scale < 0: fold the sign into q
-            qf[rb][ks] = x;
-        }
-    }
+            for (int ks = 0; ks < NKS; ++ks) {
+                u32x4_t x = {0u, 0u, 0u, 0u};
+                if (qrow(rb) < lq_b)
+                    x = *reinterpret_cast<const u32x4_t*>(
+                        qg + (int64_t)(qrow(rb) - row0) * p.q_sr + ks * 16 + 8 * hi);
+                qf[rb][ks] = x;
+            }
+    };
 
     // DMA plan of this lane: which block of a tile it fills and the byte
     // offset, from the tile's first row, of the 16 bytes it copies.  Copies
@@ -337,6 +347,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     // rows past the key range read as zeros (their scores are masked anyway).
     uint32_t dma_voff[DPW];
     int dma_dst[DPW];
+    int dma_delta[DPW];                  // dma_voff[t] - dma_voff[0], uniform
     const bool dma_is_v = wave * DPW >= L::BLOCKS;   // waves copy K or V
     const int64_t dma_sr = dma_is_v ? p.v_sr : p.k_sr;
     const uint16_t* dma_base = dma_is_v ? vg : kg;
@@ -359,11 +370,17 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         dma_voff[t] = (uint32_t)(((int64_t)r * dma_sr + c) * 2);
         dma_dst[t] = (dma_is_v ? L::ELEMS : 0) + bi * 512;
     }
+    // Only the first offset stays in a vector register; the others differ
+    // from it by amounts that are the same for every lane of the wave.
+#pragma unroll
+    for (int t = 0; t < DPW; ++t)
+        dma_delta[t] = __builtin_amdgcn_readfirstlane((int)(dma_voff[t] - dma_voff[0]));
+    const uint32_t dma_voff0 = dma_voff[0];
     // Tiles past the last one get an empty range: their copies read nothing
     // and write zeros, so every step issues the same copies and waits for
     // the same counts.
     auto tile_rsrc = [&](int kt) {
-        const int rows = kt < n_kt ? min(lk_b - kt * BN, BN) : 0;
+        const int rows = kt < kt1 ? min(lk_b - kt * BN, BN) : 0;
         const int bytes = __builtin_amdgcn_readfirstlane((int)(rows * dma_sr * 2));
         return __builtin_amdgcn_make_buffer_rsrc(
             (void*)(dma_base + (int64_t)kt * BN * dma_sr), (short)0, bytes,
@@ -372,7 +389,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     auto issue_part = [&](auto rsrc, lds16_t* stage, int t) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rsrc, (__attribute__((address_space(3))) void*)(stage + dma_dst[t]), 16,
-            dma_voff[t], 0, 0, 0);
+            dma_voff0 + (uint32_t)dma_delta[t], 0, 0, 0);
     };
     auto issue_tile = [&](int kt, lds16_t* stage) {
         const auto rsrc = tile_rsrc(kt);
@@ -437,7 +454,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     auto mask_cur = [&](int kt) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            const int lim = my_last_key[rb] - (kt * BN + 32 * kq + 4 * hi);
+            const int lim = last_key(rb) - (kt * BN + 32 * kq + 4 * hi);
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 if (8 * (e >> 2) + (e & 3) > lim) s_cur[rb][e] = -__builtin_inff();
@@ -652,11 +669,11 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     // Stage of tile t, picked without a runtime index into the ring.
     auto stage_of = [&](int t) {
         const int sl = t % STAGES;
-        lds16_t* x = st.s[0];
-        if (sl == 1) x = st.s[1];
-        if (sl == 2) x = st.s[2];
-        if (sl == 3) x = st.s[3];
-        if (sl == 4) x = st.s[4];
+        lds16_t* x = ring<D, 0>();
+        if (sl == 1) x = ring<D, 1>();
+        if (sl == 2) x = ring<D, 2>();
+        if (sl == 3) x = ring<D, 3>();
+        if (sl == 4) x = ring<D, 4>();
         return x;
     };
 
@@ -669,15 +686,15 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         n_full = min(n_full, lim > 0 ? lim / BN : 0);
     }
 
-    // Step j (0 <= j <= n_kt - 2): tile t lives in stage t % STAGES.  K of
-    // tile j+1 and V of tile j-1 are read here.  The stage refilled here,
+    // Step j (0 <= j <= n_kt - 2) works on tile kt0 + j, which lives in stage
+    // j % STAGES.  K of tile j+1 and V of tile j-1 are read here.  The stage refilled here,
     // (j + AHEAD) % STAGES = (j-2) % STAGES, was last read (V of tile j-2)
     // one step ago, and those fragments were consumed by products of that
     // step, so every wave is done with it once it reaches this step's
     // barrier.
     //   steady: stage S = j % STAGES known at compile time, no mask; FIRST
     //           (j == 0) has no P(j-1) V(j-1).
-    //   masked: any j >= n_full, stages picked at run time.
+    //   masked: any kt0 + j >= n_full, stages picked at run time.
     auto steady = [&](int j, auto SI, auto FIRST) {
         constexpr int S = decltype(SI)::value;
         constexpr bool first = decltype(FIRST)::value;
@@ -685,13 +702,17 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         // (tiles j+2 .. j+AHEAD-1) are pending
         wait_vm<(AHEAD - 2) * DPW>();
         __builtin_amdgcn_s_barrier();
+        // fragment addresses are formed here each step, not kept live per
+        // stage across the loop
+        asm volatile("" : "+v"(k_off));
+        asm volatile("" : "+v"(v_off));
         u32x4_t kf[NKS];
-        read_k(st.s[(S + 1) % STAGES], kf);
-        if constexpr (!first) read_v(st.s[(S + STAGES - 1) % STAGES]);
+        read_k(ring<D, (S + 1) % STAGES>(), kf);
+        if constexpr (!first) read_v(ring<D, (S + STAGES - 1) % STAGES>());
         f32x16_t s_new[2];
-        compute(j, std::true_type(), std::integral_constant<bool, !first>(),
+        compute(kt0 + j, std::true_type(), std::integral_constant<bool, !first>(),
                 std::false_type(), std::integral_constant<bool, first>(), kf,
-                s_new, j + AHEAD, st.s[(S + AHEAD) % STAGES]);
+                s_new, kt0 + j + AHEAD, ring<D, (S + AHEAD) % STAGES>());
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s_cur[rb] = s_new[rb];
     };
@@ -702,8 +723,8 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         read_k(stage_of(j + 1), kf);
         if (j > 0) read_v(stage_of(j - 1));   // else P(j-1) = 0 and V = 0
         f32x16_t s_new[2];
-        compute(j, std::true_type(), std::true_type(), std::true_type(),
-                std::false_type(), kf, s_new, j + AHEAD, stage_of(j + AHEAD));
+        compute(kt0 + j, std::true_type(), std::true_type(), std::true_type(),
+                std::false_type(), kf, s_new, kt0 + j + AHEAD, stage_of(j + AHEAD));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s_cur[rb] = s_new[rb];
     };
@@ -711,13 +732,22 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     if (n_kt > 0) {
         // prologue: tiles 0 .. AHEAD-1 in flight; wait for tile 0 and
         // compute S(0)
-#pragma unroll
-        for (int t = 0; t < AHEAD; ++t) issue_tile(t, st.s[t]);
+        issue_tile(kt0, ring<D, 0>());
+        load_q();
+        issue_tile(kt0 + 1, ring<D, 1>());
+        issue_tile(kt0 + 2, ring<D, 2>());
+        static_assert(AHEAD == 3, "prologue copies");
         wait_vm<(AHEAD - 1) * DPW>();    // tiles 1 .. AHEAD-1 may be pending
+        if (p.negate_q) {                // scale < 0: fold the sign into q
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] ^= 0x80008000u;
+        }
         __builtin_amdgcn_s_barrier();
         {
             u32x4_t kf[NKS];
-            read_k(st.s[0], kf);
+            read_k(ring<D, 0>(), kf);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
                 s_cur[rb] = f32x16_t{};
@@ -729,7 +759,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         static_assert(STAGES == 5, "unrolling below");
         // unmasked steps 0 .. n_un-1: step 0, then rounds of STAGES steps
         // starting at stage 1, then the remainder
-        const int n_un = min(n_full, n_kt - 1);
+        const int n_un = max(0, min(n_full - kt0, n_kt - 1));
         int j = 0;
         if (n_un >= 1) steady(j++, I0(), std::true_type());
         for (; j + STAGES <= n_un; j += STAGES) {
@@ -759,12 +789,12 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             u32x4_t kf_unused[NKS];
             f32x16_t s_unused[2];
             if (jl > 0) read_v(stage_of(jl - 1));
-            if (jl >= n_full)
-                compute(jl, std::false_type(), std::true_type(), std::true_type(),
-                        std::false_type(), kf_unused, s_unused, 0, st.s[0]);
+            if (kt0 + jl >= n_full)
+                compute(kt0 + jl, std::false_type(), std::true_type(), std::true_type(),
+                        std::false_type(), kf_unused, s_unused, 0, ring<D, 0>());
             else
-                compute(jl, std::false_type(), std::true_type(), std::false_type(),
-                        std::false_type(), kf_unused, s_unused, 0, st.s[0]);
+                compute(kt0 + jl, std::false_type(), std::true_type(), std::false_type(),
+                        std::false_type(), kf_unused, s_unused, 0, ring<D, 0>());
             read_v(stage_of(jl));
             pv_last();
         }
@@ -779,15 +809,15 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     constexpr int BPW = 2 * NDB / KQ;    // output blocks per wave
     __syncthreads();                     // every wave is done with the ring
     auto slot_acc = [&](int w) {
-        lds16_t* base = st.s[0];
+        lds16_t* base = ring<D, 0>();
         const int si = w / SPS;
-        if (si == 1) base = st.s[1];
-        if (si == 2) base = st.s[2];
-        if (si == 3) base = st.s[3];
+        if (si == 1) base = ring<D, 1>();
+        if (si == 2) base = ring<D, 2>();
+        if (si == 3) base = ring<D, 3>();
         return reinterpret_cast<lds_f4_t*>(base) + (w % SPS) * (L::ACC / 4) * 64;
     };
     auto stat = [&](int w, int rb, int k) {
-        return reinterpret_cast<lds_f32_t*>(st.s[STAGES - 1]) +
+        return reinterpret_cast<lds_f32_t*>(ring<D, STAGES - 1>()) +
                ((w * 2 + rb) * 3 + k) * 64;
     };
     {
@@ -808,7 +838,12 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     }
     __syncthreads();
 
-    auto finish = [&](const int bi) {
+    // Merged result of output block bi of this row half, relative to mu.
+    struct Block {
+        float mu, lf, lrf;
+        f32x16_t o;
+    };
+    auto combine = [&](const int bi) {
         const int rb = bi / NDB, db = bi % NDB;
         float mq[KQ];
         float mt = -__builtin_inff();
@@ -817,54 +852,136 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             mq[q] = stat(rh + 2 * q, rb, 0)[lane];
             mt = max2(mt, mq[q]);
         }
-        const float mu = mt == -__builtin_inff() ? 0.0f : mt;
-        float lf = 0.0f, lrf = 0.0f;
-        f32x16_t o = f32x16_t{};
+        Block r;
+        r.mu = mt == -__builtin_inff() ? 0.0f : mt;
+        r.lf = 0.0f;
+        r.lrf = 0.0f;
+        r.o = f32x16_t{};
 #pragma unroll
         for (int q = 0; q < KQ; ++q) {
             const int w = rh + 2 * q;
-            const float f = fast_exp2(mq[q] - mu);
-            lf += stat(w, rb, 1)[lane] * f;
-            lrf += stat(w, rb, 2)[lane] * f;
+            const float f = fast_exp2(mq[q] - r.mu);
+            r.lf += stat(w, rb, 1)[lane] * f;
+            r.lrf += stat(w, rb, 2)[lane] * f;
             const lds_f4_t* a = slot_acc(w) + ((rb * NDB + db) * 4) * 64 + lane;
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
                 const f32x4_t x = a[gg * 64];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[4 * gg + i] += x[i] * f;
+                for (int i = 0; i < 4; ++i) r.o[4 * gg + i] += x[i] * f;
             }
         }
+        return r;
+    };
+    auto store = [&](const int bi, const Block& r) {
+        const int rb = bi / NDB, db = bi % NDB;
         // O is normalised by the sum of the rounded P, LSE uses the fp32 sum
         // where there is one.
-        const float ln = lrf + partner(lrf);
-        const float lt = Mma<Tin>::kFp32Sum ? lf + partner(lf) : ln;
-        if (row_ok[rb]) {
+        const float ln = r.lrf + partner(r.lrf);
+        const float lt = Mma<Tin>::kFp32Sum ? r.lf + partner(r.lf) : ln;
+        if (qrow(rb) < lq_b) {
             const float inv = ln > 0.0f ? 1.0f / ln : 0.0f;
             const int64_t orow = (packed ? 0 : (int64_t)b * p.o_sb) +
                                  (int64_t)h * p.o_sh +
-                                 (int64_t)(q0 + qrow[rb]) * p.o_sr;
+                                 (int64_t)(q0 + qrow(rb)) * p.o_sr;
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
                 const int d0 = db * 32 + 8 * gg + 4 * hi;
-                Epi<Tout>::store4(p.o, orow + d0, o[4 * gg] * inv,
-                                  o[4 * gg + 1] * inv, o[4 * gg + 2] * inv,
-                                  o[4 * gg + 3] * inv);
+                Epi<Tout>::store4(p.o, orow + d0, r.o[4 * gg] * inv,
+                                  r.o[4 * gg + 1] * inv, r.o[4 * gg + 2] * inv,
+                                  r.o[4 * gg + 3] * inv);
             }
             if (db == 0 && p.lse != nullptr && hi == 0) {
                 const float lse = lt > 0.0f
-                                      ? (mu + __log2f(lt)) * 0.69314718055994530942f
+                                      ? (r.mu + __log2f(lt)) * 0.69314718055994530942f
                                       : -__builtin_inff();
                 const int64_t li =
-                    packed ? (int64_t)h * p.cu_q[p.batch] + q0 + qrow[rb]
-                           : ((int64_t)b * p.hq + h) * p.lq + qrow[rb];
+                    packed ? (int64_t)h * p.cu_q[p.batch] + q0 + qrow(rb)
+                           : ((int64_t)b * p.hq + h) * p.lq + qrow(rb);
                 p.lse[li] = lse;
             }
         }
     };
-    // output blocks bi = kq*BPW .. kq*BPW + BPW - 1
+    // output blocks bi = kq*BPW + i of this wave
+    Block blk[BPW];
 #pragma unroll
-    for (int bi = 0; bi < 2 * NDB; ++bi)
-        if (bi / BPW == kq) finish(bi);
+    for (int i = 0; i < BPW; ++i) blk[i] = combine(kq * BPW + i);
+    if (nchunks == 1) {
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) store(kq * BPW + i, blk[i]);
+        return;
+    }
+    // Split q-tile (two chunks).  Every chunk stores its partial result (o,
+    // mu, lf, lrf per lane of each output block); the chunk that counts last
+    // merges the other's with its own by the same rule, stores O and LSE and
+    // resets the counter for the next call.
+    constexpr int kMaxChunks = 2;
+    constexpr int kFields = 19;          // o[16], mu, lf, lrf
+    const int64_t tile_id = ((int64_t)b * p.hq + h) * p.split_tiles +
+                            (n_qtiles - 1 - qtile);   // split q-tiles only
+    auto part = [&](int c, int bi, int k) {   // chunk, row half, block, field
+        return p.split_ws +
+               ((((tile_id * kMaxChunks + c) * 2 + rh) * (2 * NDB) + bi) * kFields + k) *
+                   64 +
+               lane;
+    };
+    // Device-coherent accesses, no cache-wide fences: the partials are
+    // written and read as device-scope relaxed atomics, the stores have
+    // completed (vmcnt 0) before any wave passes the barrier ahead of the
+    // count, and the count is a device-scope atomic.
+    auto put = [&](float* a, float x) {
+        __hip_atomic_store(a, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto get = [&](float* a) {
+        return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+        const int bi = kq * BPW + i;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) put(part(chunk, bi, k), blk[i].o[k]);
+        put(part(chunk, bi, 16), blk[i].mu);
+        put(part(chunk, bi, 17), blk[i].lf);
+        put(part(chunk, bi, 18), blk[i].lrf);
+    }
+    wait_vm<0>();                        // this wave's partial is in memory
+    __syncthreads();
+    lds_f32_t* flag = reinterpret_cast<lds_f32_t*>(ring<D, STAGES - 1>()) +
+                      (L::STAGE / 2 - 1);   // last word of the stage
+    if (tid == 0) {
+        const int before = __hip_atomic_fetch_add(p.split_cnt + tile_id, 1,
+                                                  __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        *flag = before == nchunks - 1 ? 1.0f : 0.0f;
+    }
+    __syncthreads();
+    if (*flag == 0.0f) return;           // the other chunk finishes the q-tile
+    // chunk 0's partial first and chunk 1's second, whichever work-group
+    // merges, so that repeated calls give identical bits
+    const int other = 1 - chunk;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+        const int bi = kq * BPW + i;
+        Block x;
+        x.mu = get(part(other, bi, 16));
+        x.lf = get(part(other, bi, 17));
+        x.lrf = get(part(other, bi, 18));
+#pragma unroll
+        for (int k = 0; k < 16; ++k) x.o[k] = get(part(other, bi, k));
+        const Block& a = chunk == 0 ? blk[i] : x;
+        const Block& c = chunk == 0 ? x : blk[i];
+        Block r;
+        r.mu = max2(a.mu, c.mu);
+        const float fa = fast_exp2(a.mu - r.mu), fc = fast_exp2(c.mu - r.mu);
+        r.lf = a.lf * fa + c.lf * fc;
+        r.lrf = a.lrf * fa + c.lrf * fc;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) r.o[k] = a.o[k] * fa + c.o[k] * fc;
+        store(bi, r);
+    }
+    if (tid == 0)                        // ready for the next call
+        __hip_atomic_store(p.split_cnt + tile_id, 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Grid: blockIdx.x = item * (hq * batch) + (batch, head) index, so that
@@ -875,17 +992,6 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 template <int D, typename Tin, typename Tout, bool CAUSAL>
 __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn_fwd_mfma_kernel(
     FwdParams p, int n_qtiles, int pair) {
-    __shared__ __attribute__((aligned(16))) uint16_t st0[Layout<D>::STAGE];
-    __shared__ __attribute__((aligned(16))) uint16_t st1[Layout<D>::STAGE];
-    __shared__ __attribute__((aligned(16))) uint16_t st2[Layout<D>::STAGE];
-    __shared__ __attribute__((aligned(16))) uint16_t st3[Layout<D>::STAGE];
-    __shared__ __attribute__((aligned(16))) uint16_t st4[Layout<D>::STAGE];
-    Stages<D> st;
-    st.s[0] = (lds16_t*)st0;
-    st.s[1] = (lds16_t*)st1;
-    st.s[2] = (lds16_t*)st2;
-    st.s[3] = (lds16_t*)st3;
-    st.s[4] = (lds16_t*)st4;
     const int bh_count = p.hq * p.batch;
     const int item = (int)blockIdx.x / bh_count;
     const int bh = (int)blockIdx.x - item * bh_count;
@@ -893,7 +999,19 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
     const int b = bh / p.hq;
     // q-tiles of this work-group (one call site keeps the code compact)
     int tiles[2] = {item, -1};
-    if (CAUSAL) {
+    int chunk = 0, nchunks = 1;
+    if (CAUSAL && p.split_tiles > 0) {
+        // heaviest first: the two chunks of each of the split_tiles last
+        // q-tiles, then the other q-tiles
+        const int hs = p.split_tiles;
+        if (item < 2 * hs) {
+            tiles[0] = n_qtiles - 1 - item / 2;
+            chunk = item & 1;
+            nchunks = 2;
+        } else {
+            tiles[0] = n_qtiles - 1 - hs - (item - 2 * hs);
+        }
+    } else if (CAUSAL) {
         if (pair == 2) {
             // first half of the grid heaviest-first, second half
             // lightest-first: work-groups i and i + grid/2, which the
@@ -907,7 +1025,8 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
     }
     for (int it = 0; it < 2 && tiles[it] >= 0; ++it) {
         if (it > 0) __syncthreads();     // the LDS stages are reused
-        attend_qtile<D, Tin, Tout, CAUSAL>(p, tiles[it], h, b, st);
+        attend_qtile<D, Tin, Tout, CAUSAL>(p, tiles[it], h, b, chunk, nchunks,
+                                           n_qtiles);
     }
 }
 
@@ -919,7 +1038,8 @@ hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
     const int pair = !p.causal ? 0
                      : p.causal_pairs >= 0 ? p.causal_pairs
                      : (Layout<D>::WG_PER_CU == 2 ? 2 : 1);
-    const int items = pair == 1 ? (n_qtiles + 1) / 2 : n_qtiles;
+    const int items = (p.causal && p.split_tiles > 0) ? n_qtiles + p.split_tiles
+                      : pair == 1 ? (n_qtiles + 1) / 2 : n_qtiles;
     const int64_t blocks = (int64_t)items * p.hq * p.batch;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (p.causal)
@@ -931,6 +1051,37 @@ hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
                            dim3((unsigned)blocks), dim3(Layout<D>::THREADS), 0,
                            stream, p, n_qtiles, 0);
     return hipGetLastError();
+}
+
+// Causal key-split plan (host): how many of the last q-tiles of every
+// (batch, head) to process as two key chunks, so that no work-group's item is
+// much longer than the average work per resident work-group.  0 = none.
+template <int D>
+int split_tiles(const FwdParams& p, int cus) {
+    using L = Layout<D>;
+    if (!p.causal || p.cu_q != nullptr || p.lq <= 0 || p.lk <= 0) return 0;
+    const int n = (p.lq + kBM - 1) / kBM;
+    auto n_kt = [&](int t) {
+        const int64_t kend = std::min<int64_t>(p.lk, (int64_t)(t + 1) * kBM + p.lk - p.lq);
+        return kend > 0 ? (int)((kend + L::BN - 1) / L::BN) : 0;
+    };
+    int64_t total = 0;
+    for (int t = 0; t < n; ++t) total += n_kt(t);
+    total *= (int64_t)p.batch * p.hq;
+    const double avg = (double)total / ((double)cus * L::WG_PER_CU);
+    const int maxk = n_kt(n - 1);
+    if (maxk < 8 || maxk <= 1.5 * avg) return 0;
+    int hs = 0;
+    while (hs < n && 2 * n_kt(n - 1 - hs) > maxk) ++hs;
+    return hs;
+}
+
+// Workspace of a key-split launch: floats per split q-tile, in the order of
+// the kernel's partial results (2 chunks x 2 row halves x output blocks x 19
+// fields x 64 lanes).
+template <int D>
+constexpr int64_t split_floats_per_tile() {
+    return 2 * 2 * (2 * Layout<D>::NDB) * 19 * 64;
 }
 
 template <int D>

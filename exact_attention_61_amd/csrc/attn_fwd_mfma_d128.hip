@@ -8,4 +8,8 @@ hipError_t launch_mfma_d128(const FwdParams& p, int in_dtype, int out_dtype,
     return launch_d<128>(p, in_dtype, out_dtype, stream);
 }
 
+int split_tiles_d128(const FwdParams& p, int cus) { return split_tiles<128>(p, cus); }
+
+int64_t split_floats_per_tile_d128() { return split_floats_per_tile<128>(); }
+
 }  // namespace mi_attn

@@ -27,6 +27,14 @@ struct FwdParams {
     int32_t negate_q;                // 1 when scale < 0 (fold the sign into q)
     int32_t causal;
     int32_t causal_pairs;            // causal q-tile order (0, 1, 2; -1 default)
+    // Key-split of heavy causal q-tiles: the split_tiles last q-tiles of
+    // every (batch, head) are processed as two key chunks by two work-groups;
+    // the later one merges the other's partial result from split_ws (indexed
+    // by (batch, head, q-tile, chunk)) and resets the q-tile's counter in
+    // split_cnt.  0 = no split (split_ws, split_cnt unused).
+    int32_t split_tiles;
+    float* split_ws;
+    int32_t* split_cnt;
 };
 
 // Storage tags for the element types (16-bit values are kept as raw bits).
@@ -79,5 +87,11 @@ hipError_t launch_mfma_d64(const FwdParams& p, int in_dtype, int out_dtype,
                           hipStream_t stream);
 hipError_t launch_mfma_d128(const FwdParams& p, int in_dtype, int out_dtype,
                            hipStream_t stream);
+// Key-split plan of the MFMA kernel (q-tiles to split per (batch, head)) and
+// the workspace floats each split q-tile needs.
+int split_tiles_d64(const FwdParams& p, int cus);
+int split_tiles_d128(const FwdParams& p, int cus);
+int64_t split_floats_per_tile_d64();
+int64_t split_floats_per_tile_d128();
 
 }  // namespace mi_attn

@@ -9,6 +9,9 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "../../include/mi_attn.h"
 #include "common.hpp"
@@ -51,6 +54,84 @@ int causal_pairs_setting() {
         return (x >= 0 && x <= 2) ? x : -1;
     }();
     return v;
+}
+
+// MI_ATTN_SPLIT=1 turns on the key-split of heavy causal q-tiles (read on
+// every call).  Off by default: at the sizes measured so far the extra
+// work-groups' fixed cost outweighs the better balance.
+bool split_enabled() {
+    const char* e = std::getenv("MI_ATTN_SPLIT");
+    return e != nullptr && std::strcmp(e, "1") == 0;
+}
+
+int cu_count(int dev) {
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess || cus <= 0)
+        cus = 256;
+    cache[dev] = cus;
+    return cus;
+}
+
+// Workspace of the causal key-split, one per device, in kSplitRegions
+// regions used in turn, one per call: calls in flight at once (several
+// streams, or one graph's launches) use different regions as long as at most
+// kSplitRegions of them overlap.  A region's counters are back at zero when
+// its launch ends.  The workspace grows outside stream capture only
+// (allocation and the one-time zeroing of the counters are not capturable);
+// a capturing call that needs more than it has runs without the split.  It
+// is held until the process ends.
+constexpr int kSplitRegions = 4;
+
+struct SplitWs {
+    float* ws = nullptr;
+    int32_t* cnt = nullptr;
+    int64_t region_floats = 0, region_ints = 0;
+    unsigned next = 0;
+};
+
+bool split_workspace(hipStream_t stream, int64_t ws_floats, int64_t cnt_ints,
+                     float** ws, int32_t** cnt) {
+    static std::mutex mu;
+    static std::map<int, SplitWs> table;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    std::lock_guard<std::mutex> lock(mu);
+    SplitWs& w = table[dev];
+    if (w.region_floats < ws_floats || w.region_ints < cnt_ints) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess ||
+            cs != hipStreamCaptureStatusNone)
+            return false;
+        // every earlier launch on this device may still use the old regions
+        if (hipDeviceSynchronize() != hipSuccess) return false;
+        if (w.ws) (void)hipFree(w.ws);
+        if (w.cnt) (void)hipFree(w.cnt);
+        w = SplitWs{};
+        float* nws = nullptr;
+        int32_t* ncnt = nullptr;
+        if (hipMalloc(&nws, kSplitRegions * ws_floats * sizeof(float)) != hipSuccess)
+            return false;
+        if (hipMalloc(&ncnt, kSplitRegions * cnt_ints * sizeof(int32_t)) != hipSuccess ||
+            hipMemset(ncnt, 0, kSplitRegions * cnt_ints * sizeof(int32_t)) != hipSuccess) {
+            (void)hipFree(nws);
+            if (ncnt) (void)hipFree(ncnt);
+            return false;
+        }
+        w.ws = nws;
+        w.cnt = ncnt;
+        w.region_floats = ws_floats;
+        w.region_ints = cnt_ints;
+    }
+    const unsigned r = w.next++ % kSplitRegions;
+    *ws = w.ws + r * w.region_floats;
+    *cnt = w.cnt + r * w.region_ints;
+    return true;
 }
 
 mi_attn_strides_t default_strides(bool packed, int64_t heads, int64_t rows,
@@ -138,6 +219,21 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
     p.causal_pairs = causal_pairs_setting();
 
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    p.split_tiles = 0;
+    if (!use_scalar_kernel() && split_enabled() && causal && !packed) {
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            const int cus = cu_count(dev);
+            const int hs = head_dim == 64 ? mi_attn::split_tiles_d64(p, cus)
+                                          : mi_attn::split_tiles_d128(p, cus);
+            const int64_t per = head_dim == 64 ? mi_attn::split_floats_per_tile_d64()
+                                               : mi_attn::split_floats_per_tile_d128();
+            const int64_t tiles = (int64_t)batch * hq * hs;
+            if (hs > 0 && split_workspace(st, tiles * per, tiles, &p.split_ws,
+                                          &p.split_cnt))
+                p.split_tiles = hs;
+        }
+    }
     const hipError_t err =
         use_scalar_kernel()
             ? mi_attn::launch_simple(p, (int)in_dtype, (int)out_dtype,

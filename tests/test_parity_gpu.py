@@ -316,3 +316,37 @@ def test_repeat_runs_are_bit_identical():
     o1, l1 = run_gpu(inp["q"], inp["k"], inp["v"], causal=True, scale=0.125)
     o2, l2 = run_gpu(inp["q"], inp["k"], inp["v"], causal=True, scale=0.125)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
+# Key-split of heavy causal q-tiles (MI_ATTN_SPLIT=1): two work-groups take
+# the two key halves of each heavy q-tile and the later one merges the
+# other's partial result.  Head counts that are not multiples of 8 put the
+# two halves on different XCDs, so the hand-over is checked across them.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("b,h,lq,lk,d,dtype", [
+    (1, 3, 1024, 1024, 64, F16),
+    (2, 5, 1024, 1024, 64, BF16),
+    (1, 5, 1024, 1024, 128, BF16),
+    (1, 3, 700, 1100, 64, F16),
+    (1, 2, 2048, 2048, 128, F16),
+])
+def test_key_split_causal(monkeypatch, b, h, lq, lk, d, dtype):
+    monkeypatch.setenv("MI_ATTN_SPLIT", "1")
+    note(f"key split b{b} h{h} lq{lq} lk{lk} d{d} {dtype}")
+    dense_case(b, h, h, lq, lk, d, dtype, True)
+
+
+def test_key_split_repeat_runs_are_bit_identical(monkeypatch):
+    monkeypatch.setenv("MI_ATTN_SPLIT", "1")
+    note("key split determinism")
+    inp = workloads.make("causal_b2h16", seed=1)
+    o1, l1 = run_gpu(inp["q"], inp["k"], inp["v"], causal=True, scale=0.125)
+    o2, l2 = run_gpu(inp["q"], inp["k"], inp["v"], causal=True, scale=0.125)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o_ref, l_ref = oracle.attention(workloads.to_f64(inp["q"]),
+                                    workloads.to_f64(inp["k"]),
+                                    workloads.to_f64(inp["v"]), scale=0.125,
+                                    causal=True)
+    compare(o1, l1, o_ref, l_ref)
