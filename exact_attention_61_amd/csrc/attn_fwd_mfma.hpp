@@ -277,12 +277,16 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     using I4 = std::integral_constant<int, 4>;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar
     const int kq = wave >> 1;            // key group of every tile
     const int rh = wave & 1;             // row half of the q-tile
-    const int hi = lane >> 5;            // which half of the wave
-    const int col = lane & 31;           // the query row this lane owns
+    // Lane indices.  Re-pinned (refresh_lane) where the code after the key
+    // loop starts, so offsets derived from them are recomputed there rather
+    // than kept in registers across the loop.
+    int lane = tid & 63;
+    int hi = lane >> 5;                  // which half of the wave
+    int col = lane & 31;                 // the query row this lane owns
+    auto refresh_lane = [&]() { asm volatile("" : "+v"(lane), "+v"(hi), "+v"(col)); };
 
     int q0 = 0, lq_b = p.lq, k0 = 0, lk_b = p.lk;
     const bool packed = p.cu_q != nullptr;
@@ -321,7 +325,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     const int wrow0 = row0 + 64 * rh;    // first row of this wave
     // This lane's row of block rb (sequence-local) and the last key it may
     // see; recomputed where needed rather than held across the key loop.
-    auto qrow = [&](int rb) { return wrow0 + 32 * rb + (int)(threadIdx.x & 31); };
+    auto qrow = [&](int rb) { return wrow0 + 32 * rb + col; };
     auto last_key = [&](int rb) {
         return CAUSAL ? min(lk_b - 1, qrow(rb) + diag) : lk_b - 1;
     };
@@ -719,6 +723,9 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     auto masked = [&](int j) {
         wait_vm<(AHEAD - 2) * DPW>();
         __builtin_amdgcn_s_barrier();
+        refresh_lane();
+        asm volatile("" : "+v"(k_off));
+        asm volatile("" : "+v"(v_off));
         u32x4_t kf[NKS];
         read_k(stage_of(j + 1), kf);
         if (j > 0) read_v(stage_of(j - 1));   // else P(j-1) = 0 and V = 0
@@ -786,6 +793,9 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         {
             const int jl = n_kt - 1;
             wait_vm_lgkm0<0>();
+            refresh_lane();
+            asm volatile("" : "+v"(k_off));
+            asm volatile("" : "+v"(v_off));
             u32x4_t kf_unused[NKS];
             f32x16_t s_unused[2];
             if (jl > 0) read_v(stage_of(jl - 1));
@@ -808,6 +818,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     constexpr int SPS = L::SLOTS_PER_STAGE;
     constexpr int BPW = 2 * NDB / KQ;    // output blocks per wave
     __syncthreads();                     // every wave is done with the ring
+    refresh_lane();
     auto slot_acc = [&](int w) {
         lds16_t* base = ring<D, 0>();
         const int si = w / SPS;
@@ -991,7 +1002,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 // tile of an odd count runs alone.
 template <int D, typename Tin, typename Tout, bool CAUSAL>
 __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn_fwd_mfma_kernel(
-    FwdParams p, int n_qtiles, int pair) {
+    FwdParams p, int n_qtiles, int pair, SplitOrder so) {
     const int bh_count = p.hq * p.batch;
     const int item = (int)blockIdx.x / bh_count;
     const int bh = (int)blockIdx.x - item * bh_count;
@@ -1001,16 +1012,12 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
     int tiles[2] = {item, -1};
     int chunk = 0, nchunks = 1;
     if (CAUSAL && p.split_tiles > 0) {
-        // heaviest first: the two chunks of each of the split_tiles last
-        // q-tiles, then the other q-tiles
-        const int hs = p.split_tiles;
-        if (item < 2 * hs) {
-            tiles[0] = n_qtiles - 1 - item / 2;
-            chunk = item & 1;
-            nchunks = 2;
-        } else {
-            tiles[0] = n_qtiles - 1 - hs - (item - 2 * hs);
-        }
+        // longest item first: the chunks of the split_tiles last q-tiles and
+        // the other q-tiles, in the order the host sorted them
+        const int e = so.e[item];
+        tiles[0] = e >> 1;
+        chunk = e & 1;
+        nchunks = tiles[0] >= n_qtiles - p.split_tiles ? 2 : 1;
     } else if (CAUSAL) {
         if (pair == 2) {
             // first half of the grid heaviest-first, second half
@@ -1031,7 +1038,8 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
 }
 
 template <int D, typename Tin, typename Tout>
-hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
+hipError_t launch_typed(const FwdParams& p, const SplitOrder& so,
+                        hipStream_t stream) {
     const int n_qtiles = (p.lq + kBM - 1) / kBM;
     // causal q-tile order: with two resident work-groups per CU, grid halves
     // heaviest-first and lightest-first; with one, q-tile pairs
@@ -1045,11 +1053,11 @@ hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
     if (p.causal)
         hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true>),
                            dim3((unsigned)blocks), dim3(Layout<D>::THREADS), 0,
-                           stream, p, n_qtiles, pair);
+                           stream, p, n_qtiles, pair, so);
     else
         hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, false>),
                            dim3((unsigned)blocks), dim3(Layout<D>::THREADS), 0,
-                           stream, p, n_qtiles, 0);
+                           stream, p, n_qtiles, 0, so);
     return hipGetLastError();
 }
 
@@ -1073,7 +1081,35 @@ int split_tiles(const FwdParams& p, int cus) {
     if (maxk < 8 || maxk <= 1.5 * avg) return 0;
     int hs = 0;
     while (hs < n && 2 * n_kt(n - 1 - hs) > maxk) ++hs;
+    if (n + hs > SplitOrder::kMaxItems) return 0;
     return hs;
+}
+
+// Items of a split launch sorted longest first (ties: later q-tile first):
+// entry = q-tile * 2 + chunk; the split_tiles last q-tiles have two chunks.
+template <int D>
+void split_order(const FwdParams& p, int hs, SplitOrder& so) {
+    using L = Layout<D>;
+    const int n = (p.lq + kBM - 1) / kBM;
+    auto n_kt = [&](int t) {
+        const int64_t kend = std::min<int64_t>(p.lk, (int64_t)(t + 1) * kBM + p.lk - p.lq);
+        return kend > 0 ? (int)((kend + L::BN - 1) / L::BN) : 0;
+    };
+    struct It { int len, e; };
+    It items[SplitOrder::kMaxItems];
+    int m = 0;
+    for (int t = n - 1; t >= 0; --t) {
+        const int k = n_kt(t);
+        if (t >= n - hs) {
+            items[m++] = {k / 2, 2 * t};           // chunk 0: [0, k/2)
+            items[m++] = {k - k / 2, 2 * t + 1};   // chunk 1: [k/2, k)
+        } else {
+            items[m++] = {k, 2 * t};
+        }
+    }
+    std::stable_sort(items, items + m,
+                     [](const It& a, const It& b) { return a.len > b.len; });
+    for (int i = 0; i < m; ++i) so.e[i] = (uint16_t)items[i].e;
 }
 
 // Workspace of a key-split launch: floats per split q-tile, in the order of
@@ -1085,14 +1121,14 @@ constexpr int64_t split_floats_per_tile() {
 }
 
 template <int D>
-hipError_t launch_d(const FwdParams& p, int in_dtype, int out_dtype,
-                    hipStream_t stream) {
+hipError_t launch_d(const FwdParams& p, const SplitOrder& so, int in_dtype,
+                    int out_dtype, hipStream_t stream) {
     if (in_dtype == 0) {
-        return out_dtype == 2 ? launch_typed<D, f16_t, float>(p, stream)
-                              : launch_typed<D, f16_t, f16_t>(p, stream);
+        return out_dtype == 2 ? launch_typed<D, f16_t, float>(p, so, stream)
+                              : launch_typed<D, f16_t, f16_t>(p, so, stream);
     }
-    return out_dtype == 2 ? launch_typed<D, bf16_t, float>(p, stream)
-                          : launch_typed<D, bf16_t, bf16_t>(p, stream);
+    return out_dtype == 2 ? launch_typed<D, bf16_t, float>(p, so, stream)
+                          : launch_typed<D, bf16_t, bf16_t>(p, so, stream);
 }
 
 }  // namespace

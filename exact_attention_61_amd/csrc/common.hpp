@@ -37,6 +37,13 @@ struct FwdParams {
     int32_t* split_cnt;
 };
 
+// Item order of a split launch, longest first: entry = q-tile * 2 + chunk.
+// A kernel argument of its own, read only by the work-group's item decode.
+struct SplitOrder {
+    static constexpr int kMaxItems = 256;
+    uint16_t e[kMaxItems];
+};
+
 // Storage tags for the element types (16-bit values are kept as raw bits).
 struct f16_t { uint16_t bits; };
 struct bf16_t { uint16_t bits; };
@@ -83,15 +90,17 @@ template <> struct OutStore<float> {
 // argument was validated by the caller.  Return the hipGetLastError() code.
 hipError_t launch_simple(const FwdParams& p, int in_dtype, int out_dtype,
                          int head_dim, hipStream_t stream);
-hipError_t launch_mfma_d64(const FwdParams& p, int in_dtype, int out_dtype,
-                          hipStream_t stream);
-hipError_t launch_mfma_d128(const FwdParams& p, int in_dtype, int out_dtype,
-                           hipStream_t stream);
+hipError_t launch_mfma_d64(const FwdParams& p, const SplitOrder& so,
+                          int in_dtype, int out_dtype, hipStream_t stream);
+hipError_t launch_mfma_d128(const FwdParams& p, const SplitOrder& so,
+                           int in_dtype, int out_dtype, hipStream_t stream);
 // Key-split plan of the MFMA kernel (q-tiles to split per (batch, head)) and
 // the workspace floats each split q-tile needs.
 int split_tiles_d64(const FwdParams& p, int cus);
 int split_tiles_d128(const FwdParams& p, int cus);
 int64_t split_floats_per_tile_d64();
+void split_order_d64(const FwdParams& p, int hs, SplitOrder& so);
+void split_order_d128(const FwdParams& p, int hs, SplitOrder& so);
 int64_t split_floats_per_tile_d128();
 
 }  // namespace mi_attn

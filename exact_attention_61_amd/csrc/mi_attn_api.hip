@@ -220,6 +220,7 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
 
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     p.split_tiles = 0;
+    mi_attn::SplitOrder so{};
     if (!use_scalar_kernel() && split_enabled() && causal && !packed) {
         int dev = 0;
         if (hipGetDevice(&dev) == hipSuccess) {
@@ -230,8 +231,11 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
                                                : mi_attn::split_floats_per_tile_d128();
             const int64_t tiles = (int64_t)batch * hq * hs;
             if (hs > 0 && split_workspace(st, tiles * per, tiles, &p.split_ws,
-                                          &p.split_cnt))
+                                          &p.split_cnt)) {
                 p.split_tiles = hs;
+                if (head_dim == 64) mi_attn::split_order_d64(p, hs, so);
+                else mi_attn::split_order_d128(p, hs, so);
+            }
         }
     }
     const hipError_t err =
@@ -239,8 +243,8 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
             ? mi_attn::launch_simple(p, (int)in_dtype, (int)out_dtype,
                                      head_dim, st)
             : head_dim == 64
-                  ? mi_attn::launch_mfma_d64(p, (int)in_dtype, (int)out_dtype, st)
-                  : mi_attn::launch_mfma_d128(p, (int)in_dtype, (int)out_dtype,
+                  ? mi_attn::launch_mfma_d64(p, so, (int)in_dtype, (int)out_dtype, st)
+                  : mi_attn::launch_mfma_d128(p, so, (int)in_dtype, (int)out_dtype,
                                               st);
     if (err != hipSuccess) {
         g_last_hip_error = (int32_t)err;
