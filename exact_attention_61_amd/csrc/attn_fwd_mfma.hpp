@@ -13,11 +13,13 @@
 // each side scaled by 2^(m_side - m)), which is how the waves that share a
 // row block merge their results at the end.
 //
-// The reference max is only replaced when a tile's max exceeds it by more
-// than a gap of 8 (log2 units), and the rescale is skipped when no row of the
-// wave needs it.  Any reference value gives the same O = u / l and LSE =
-// m + log2 l; probabilities stay below 2^8, far inside every range, and the
-// rescale of the accumulator is skipped on almost every tile.  The output is
+// The reference max of a row is set from the first tile's scores; later tiles
+// are exponentiated against it without computing their max.  Only when some
+// lane's 16 probabilities of a row sum to more than 2^10 (or overflow) does
+// the wave recompute the tile's scores, move the references of the rows whose
+// tile max exceeds them to that max and rescale.  Any reference value gives
+// the same O = u / l and LSE = m + log2 l; probabilities stay below 2^10, far
+// inside every range, and the rescale is skipped on almost every tile.  The output is
 // normalised by the sum of the probabilities as rounded for the PV product
 // (one v_dot2 per pair), so that the rounding of a dominant probability
 // cancels between numerator and denominator.  The log-sum-exp uses that sum
@@ -93,8 +95,11 @@ constexpr int kBM = 128;     // query rows per q-tile
 constexpr int kStages = 5;   // LDS ring of K/V tiles
 
 template <typename T> struct Mma;
+// Safe form of the softmax: a row's reference max moves only when a tile's
+// max exceeds it by more than this (log2 units).
+constexpr float kGap = 8.0f;
+
 template <> struct Mma<f16_t> {
-    static constexpr float kGap = 8.0f;   // reference-max lag allowed (log2)
     __device__ __forceinline__ static f32x16_t run(u32x4_t a, u32x4_t b,
                                                    f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(
@@ -119,7 +124,6 @@ template <> struct Mma<f16_t> {
     }
 };
 template <> struct Mma<bf16_t> {
-    static constexpr float kGap = 8.0f;
     __device__ __forceinline__ static f32x16_t run(u32x4_t a, u32x4_t b,
                                                    f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -404,9 +408,11 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     const float c2 = p.scale_log2;       // |scale| * log2(e)
     float m[2], l[2], lr[2];             // per row block: reference max (log2
     f32x16_t acc[2][NDB];                // domain), this lane's exp-sums, O^T
+    float nm[2];                         // -m, or 0 while m is -inf
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         m[rb] = -__builtin_inff();
+        nm[rb] = 0.0f;
         l[rb] = 0.0f;
         lr[rb] = 0.0f;                   // sum of the rounded P
 #pragma unroll
@@ -474,48 +480,6 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                     acc[rb][db] = Mma<Tin>::run(vf[db][c], p_prev[rb][c], acc[rb][db]);
     };
 
-    // Softmax of S(j) in its full form: row max (with lane ^ 32), reference
-    // update when the tile's max exceeds the reference by more than the gap,
-    // p = 2^(s*c2 - m), rounded P and row sums, rescale of l, lr and the
-    // accumulators (after the previous tile's product).  Used for a q-tile's
-    // first tile and whenever the short form below may have left range.
-    auto softmax_full = [&](u32x4_t (&p_new)[2][2]) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const f32x16_t& x = s_cur[rb];
-            const float a0 = max2(max2(x[0], x[1]), x[2]);
-            const float a1 = max2(max2(x[3], x[4]), x[5]);
-            const float a2 = max2(max2(x[6], x[7]), x[8]);
-            const float a3 = max2(max2(x[9], x[10]), x[11]);
-            const float a4 = max2(max2(x[12], x[13]), x[14]);
-            const float mx = max2(max2(max2(a0, a1), a2), max2(max2(a3, a4), x[15]));
-            const float mt = max2(mx, partner(mx)) * c2;
-            const bool grow = mt > m[rb] + Mma<Tin>::kGap;   // false if all -inf
-            const float m_new = grow ? mt : m[rb];
-            const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
-            float rs = 0.0f, rsr = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                s_cur[rb][e] = fast_exp2(fmaf(s_cur[rb][e], c2, -m_use));
-                rs += s_cur[rb][e];
-            }
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int e = 8 * c + 2 * jj;
-                    p_new[rb][c][jj] = Mma<Tin>::pack(s_cur[rb][e], s_cur[rb][e + 1]);
-                    rsr = Mma<Tin>::add_pair(p_new[rb][c][jj], rsr);
-                }
-            const float alpha = grow ? fast_exp2(m[rb] - m_new) : 1.0f;
-            l[rb] = l[rb] * alpha + (Mma<Tin>::kFp32Sum ? rs : 0.0f);
-            lr[rb] = lr[rb] * alpha + rsr;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[rb][db] *= alpha;
-            m[rb] = m_new;
-        }
-    };
-
     // One pipeline step for tile j.  The matrix products of the step -- with
     // NEXT S(j+1) = Q K(j+1)^T of row block 0, then (with PV) O += P(j-1)
     // V(j-1), then S(j+1) of row block 1 -- are spread between groups of the
@@ -523,21 +487,30 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     // Scheduling barriers keep the order, so the wave issues a product and
     // then vector work while the matrix core runs it.
     //
-    // Reference update: every lane takes the max of its own 16 scores of a
-    // row; only when some lane's max exceeds its row's reference by more than
-    // the gap (rarely, after a row's first tile) does the wave exchange the
-    // maxima with lane ^ 32, move the references of the rows whose tile max
-    // exceeds them by more than the gap, and rescale.  FULL (first tile of a
-    // q-tile): the full form, with every row's reference set from the tile.
-    auto compute = [&](int j, auto NEXT, auto PV, auto MASK, auto FULL,
+    // Short form (SAFE false): p = 2^(s*c2 - m) against the references set
+    // from the first tile, with no max of the tile at all.  The references
+    // never need to move for accuracy: the largest probability of every row
+    // is at least 1 (its first tile's max) and larger ones keep their
+    // relative precision, so only an overflow (a probability past the range
+    // of the 16-bit type, or of fp32) is wrong, and it leaves an inf in the
+    // row sums, which only grow.  The caller checks them after the last tile
+    // and redoes the q-tile in the safe form if needed.
+    //
+    // Safe form: every lane takes the max of its own 16 scores of a row;
+    // only when some lane's max exceeds its row's reference by more than
+    // kGap does the wave exchange the maxima with lane ^ 32, move the
+    // references of the rows whose tile max exceeds them by more than kGap,
+    // and rescale (the accumulators after this step's products).
+    auto compute = [&](int j, auto NEXT, auto PV, auto MASK, auto SAFE,
                        const u32x4_t (&kf)[NKS], f32x16_t (&s_next)[2],
                        int dma_kt, lds16_t* dma_stage) {
         constexpr bool next = decltype(NEXT)::value;
+        constexpr bool safe = decltype(SAFE)::value;
         constexpr int NPV = decltype(PV)::value ? 2 * NDB * 2 : 0;
         constexpr int NQK = next ? 2 * NKS : 0;
         constexpr int NM = NPV + NQK;
         constexpr int PV0 = NQK / 2;     // first PV product
-        constexpr int kGroups = 13;
+        constexpr int kGroups = safe ? 13 : 9;
         auto mfma = [&](int q) {
             if (q >= PV0 && q < PV0 + NPV) {
                 const int qp = q - PV0;
@@ -553,19 +526,57 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         };
         if constexpr (decltype(MASK)::value) mask_cur(j);
         u32x4_t p_new[2][2];             // this tile's P; p_prev stays for PV
-        if constexpr (decltype(FULL)::value) {
-            if (next) issue_tile(dma_kt, dma_stage);
+        // The copy of tile dma_kt (NEXT only), one instruction every few
+        // groups: a burst of copies from every wave at once fills the memory
+        // pipeline's queue and stalls the waves behind it.
+        auto dma_at = [&](int gi, auto rsrc) {
+            if (next) {
 #pragma unroll
-            for (int q = 0; q < NM; ++q) mfma(q);
-            softmax_full(p_new);
+                for (int t = 0; t < DPW; ++t)
+                    if (gi == 1 + t * (kGroups - 2) / DPW) issue_part(rsrc, dma_stage, t);
+            }
+        };
+        const auto rsrc = tile_rsrc(dma_kt);
+        if constexpr (!safe) {
+            // Part u (0..7) = scores 4 * (u & 3) .. +3 of row block u >> 2:
+            // group g exponentiates part g and rounds and sums part g - 1.
+            // The row sums go straight into l and lr.
+            float pe[2][4];              // probabilities of the last two parts
+#pragma unroll
+            for (int gi = 0; gi < kGroups; ++gi) {
+                if (gi < 8) {
+                    const int rb = gi >> 2, e0 = 4 * (gi & 3);
+                    float* x = pe[gi & 1];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        x[i] = fast_exp2(fmaf(s_cur[rb][e0 + i], c2, nm[rb]));
+                        pin(x[i]);       // computed in this group, not sunk
+                    }
+                    if (Mma<Tin>::kFp32Sum) {
+                        l[rb] += (x[0] + x[1]) + (x[2] + x[3]);
+                        pin(l[rb]);
+                    }
+                }
+                if (gi >= 1) {
+                    const int u = gi - 1, rb = u >> 2, c = (u >> 1) & 1, h = u & 1;
+                    const float* x = pe[u & 1];
+                    const uint32_t a = Mma<Tin>::pack(x[0], x[1]);
+                    const uint32_t d = Mma<Tin>::pack(x[2], x[3]);
+                    p_new[rb][c][2 * h] = a;
+                    p_new[rb][c][2 * h + 1] = d;
+                    lr[rb] = Mma<Tin>::add_pair(d, Mma<Tin>::add_pair(a, lr[rb]));
+                    pin(lr[rb]);
+                    pin(p_new[rb][c]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q = gi * NM / kGroups; q < (gi + 1) * NM / kGroups; ++q) mfma(q);
+                dma_at(gi, rsrc);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         } else {
-            // The copy of tile dma_kt (NEXT only), one instruction every few
-            // groups: a burst of copies from every wave at once fills the
-            // memory pipeline's queue and stalls the waves behind it.
-            const auto rsrc = tile_rsrc(dma_kt);
             float psum[2][4];
             float rsr[2][2];             // row sums of the rounded P, per chunk
-            float m_use[2];
             bool upd;                    // some reference moved (wave-uniform)
             float alpha[2] = {1.0f, 1.0f};
 #pragma unroll
@@ -584,7 +595,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                         const float a4 = max2(max2(x[12], x[13]), x[14]);
                         mt[rb] = max2(max2(max2(a0, a1), a2),
                                       max2(max2(a3, a4), x[15])) * c2;
-                        need[rb] = mt[rb] > m[rb] + Mma<Tin>::kGap;
+                        need[rb] = mt[rb] > m[rb] + kGap;
                     }
                     upd = __builtin_amdgcn_ballot_w64(need[0] || need[1]) != 0;
                     if (upd) {
@@ -592,25 +603,23 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 #pragma unroll
                         for (int rb = 0; rb < 2; ++rb) {
                             const float mr = max2(mt[rb], partner(mt[rb]));
-                            const bool grow = mr > m[rb] + Mma<Tin>::kGap;
+                            const bool grow = mr > m[rb] + kGap;
                             const float m_new = grow ? mr : m[rb];
                             alpha[rb] = grow ? fast_exp2(m[rb] - m_new) : 1.0f;
                             l[rb] *= alpha[rb];
                             lr[rb] *= alpha[rb];
                             m[rb] = m_new;
+                            nm[rb] = m_new == -__builtin_inff() ? 0.0f : -m_new;
                         }
                     }
-#pragma unroll
-                    for (int rb = 0; rb < 2; ++rb)
-                        m_use[rb] = m[rb] == -__builtin_inff() ? 0.0f : m[rb];
                 } else if (gi < 9) {
                     // p = 2^(s*c2 - m) for 4 scores of row block gi & 1
                     const int rb = (gi - 1) & 1, e0 = 4 * ((gi - 1) >> 1);
                     float pe[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        pe[i] = fast_exp2(fmaf(s_cur[rb][e0 + i], c2, -m_use[rb]));
-                        pin(pe[i]);   // computed in this group, not sunk
+                        pe[i] = fast_exp2(fmaf(s_cur[rb][e0 + i], c2, nm[rb]));
+                        pin(pe[i]);
                         s_cur[rb][e0 + i] = pe[i];
                     }
                     if (Mma<Tin>::kFp32Sum) {
@@ -618,8 +627,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                         pin(psum[rb][(gi - 1) >> 1]);
                     }
                 } else {
-                    // P^T operand of 16-key chunk c of row block rb: elements
-                    // 8c .. 8c+7 of s_cur[rb], rounded to the input type
+                    // P^T operand of 16-key chunk c of row block rb
                     const int rb = (gi - 9) >> 1, c = (gi - 9) & 1;
                     float t0 = 0.0f, t1 = 0.0f;
 #pragma unroll
@@ -635,13 +643,8 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int q = gi * NM / kGroups; q < (gi + 1) * NM / kGroups; ++q)
-                    mfma(q);
-                if (next) {
-#pragma unroll
-                    for (int t = 0; t < DPW; ++t)
-                        if (gi == 1 + t * (kGroups - 1) / DPW) issue_part(rsrc, dma_stage, t);
-                }
+                for (int q = gi * NM / kGroups; q < (gi + 1) * NM / kGroups; ++q) mfma(q);
+                dma_at(gi, rsrc);
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
@@ -699,7 +702,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     //   steady: stage S = j % STAGES known at compile time, no mask; FIRST
     //           (j == 0) has no P(j-1) V(j-1).
     //   masked: any kt0 + j >= n_full, stages picked at run time.
-    auto steady = [&](int j, auto SI, auto FIRST) {
+    auto steady = [&](int j, auto SI, auto FIRST, auto SAFE) {
         constexpr int S = decltype(SI)::value;
         constexpr bool first = decltype(FIRST)::value;
         // tile j+1 has landed once at most the copies issued after it
@@ -715,12 +718,12 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         if constexpr (!first) read_v(ring<D, (S + STAGES - 1) % STAGES>());
         f32x16_t s_new[2];
         compute(kt0 + j, std::true_type(), std::integral_constant<bool, !first>(),
-                std::false_type(), std::integral_constant<bool, first>(), kf,
-                s_new, kt0 + j + AHEAD, ring<D, (S + AHEAD) % STAGES>());
+                std::false_type(), SAFE, kf, s_new, kt0 + j + AHEAD,
+                ring<D, (S + AHEAD) % STAGES>());
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s_cur[rb] = s_new[rb];
     };
-    auto masked = [&](int j) {
+    auto masked = [&](int j, auto SAFE) {
         wait_vm<(AHEAD - 2) * DPW>();
         __builtin_amdgcn_s_barrier();
         refresh_lane();
@@ -730,85 +733,105 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         read_k(stage_of(j + 1), kf);
         if (j > 0) read_v(stage_of(j - 1));   // else P(j-1) = 0 and V = 0
         f32x16_t s_new[2];
-        compute(kt0 + j, std::true_type(), std::true_type(), std::true_type(),
-                std::false_type(), kf, s_new, kt0 + j + AHEAD, stage_of(j + AHEAD));
+        compute(kt0 + j, std::true_type(), std::true_type(), std::true_type(), SAFE,
+                kf, s_new, kt0 + j + AHEAD, stage_of(j + AHEAD));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s_cur[rb] = s_new[rb];
     };
 
-    if (n_kt > 0) {
-        // prologue: tiles 0 .. AHEAD-1 in flight; wait for tile 0 and
-        // compute S(0)
-        issue_tile(kt0, ring<D, 0>());
-        load_q();
-        issue_tile(kt0 + 1, ring<D, 1>());
-        issue_tile(kt0 + 2, ring<D, 2>());
-        static_assert(AHEAD == 3, "prologue copies");
-        wait_vm<(AHEAD - 1) * DPW>();    // tiles 1 .. AHEAD-1 may be pending
-        if (p.negate_q) {                // scale < 0: fold the sign into q
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] ^= 0x80008000u;
-        }
-        __builtin_amdgcn_s_barrier();
-        {
-            u32x4_t kf[NKS];
-            read_k(ring<D, 0>(), kf);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                s_cur[rb] = f32x16_t{};
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    s_cur[rb] = Mma<Tin>::run(kf[ks], qf[rb][ks], s_cur[rb]);
+    // The key loop: prologue, steps, last tile.  The short form first; the
+    // safe form only when the short form overflowed (see compute).
+    auto run_keys = [&](auto SAFE) {
+        if (n_kt > 0) {
+            // prologue: tiles 0 .. AHEAD-1 in flight; wait for tile 0 and
+            // compute S(0)
+            issue_tile(kt0, ring<D, 0>());
+            load_q();
+            issue_tile(kt0 + 1, ring<D, 1>());
+            issue_tile(kt0 + 2, ring<D, 2>());
+            static_assert(AHEAD == 3, "prologue copies");
+            wait_vm<(AHEAD - 1) * DPW>();    // tiles 1 .. AHEAD-1 may be pending
+            if (p.negate_q) {                // scale < 0: fold the sign into q
+    #pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+    #pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] ^= 0x80008000u;
             }
-        }
-        static_assert(STAGES == 5, "unrolling below");
-        // unmasked steps 0 .. n_un-1: step 0, then rounds of STAGES steps
-        // starting at stage 1, then the remainder
-        const int n_un = max(0, min(n_full - kt0, n_kt - 1));
-        int j = 0;
-        if (n_un >= 1) steady(j++, I0(), std::true_type());
-        for (; j + STAGES <= n_un; j += STAGES) {
-            steady(j, I1(), std::false_type());
-            steady(j + 1, I2(), std::false_type());
-            steady(j + 2, I3(), std::false_type());
-            steady(j + 3, I4(), std::false_type());
-            steady(j + 4, I0(), std::false_type());
-        }
-        // remaining unmasked steps (j < n_un), j % STAGES == 1 here
-        if (j < n_un) {
-            steady(j++, I1(), std::false_type());
-            if (j < n_un) {
-                steady(j++, I2(), std::false_type());
-                if (j < n_un) {
-                    steady(j++, I3(), std::false_type());
-                    if (j < n_un) steady(j++, I4(), std::false_type());
+            __builtin_amdgcn_s_barrier();
+            {
+                u32x4_t kf[NKS];
+                read_k(ring<D, 0>(), kf);
+    #pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    s_cur[rb] = f32x16_t{};
+    #pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+                        s_cur[rb] = Mma<Tin>::run(kf[ks], qf[rb][ks], s_cur[rb]);
                 }
             }
+            // references from the first tile's row maxima (its masked scores
+            // excluded); every step then takes the short form of the softmax
+            if (kt0 >= n_full) mask_cur(kt0);
+    #pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const f32x16_t& x = s_cur[rb];
+                const float a0 = max2(max2(x[0], x[1]), x[2]);
+                const float a1 = max2(max2(x[3], x[4]), x[5]);
+                const float a2 = max2(max2(x[6], x[7]), x[8]);
+                const float a3 = max2(max2(x[9], x[10]), x[11]);
+                const float a4 = max2(max2(x[12], x[13]), x[14]);
+                const float mx = max2(max2(max2(a0, a1), a2), max2(max2(a3, a4), x[15]));
+                m[rb] = max2(mx, partner(mx)) * c2;
+                nm[rb] = m[rb] == -__builtin_inff() ? 0.0f : -m[rb];
+            }
+            static_assert(STAGES == 5, "unrolling below");
+            // unmasked steps 0 .. n_un-1: step 0, then rounds of STAGES steps
+            // starting at stage 1, then the remainder
+            const int n_un = max(0, min(n_full - kt0, n_kt - 1));
+            int j = 0;
+            if (n_un >= 1) steady(j++, I0(), std::true_type(), SAFE);
+            for (; j + STAGES <= n_un; j += STAGES) {
+                steady(j, I1(), std::false_type(), SAFE);
+                steady(j + 1, I2(), std::false_type(), SAFE);
+                steady(j + 2, I3(), std::false_type(), SAFE);
+                steady(j + 3, I4(), std::false_type(), SAFE);
+                steady(j + 4, I0(), std::false_type(), SAFE);
+            }
+            // remaining unmasked steps (j < n_un), j % STAGES == 1 here
+            if (j < n_un) {
+                steady(j++, I1(), std::false_type(), SAFE);
+                if (j < n_un) {
+                    steady(j++, I2(), std::false_type(), SAFE);
+                    if (j < n_un) {
+                        steady(j++, I3(), std::false_type(), SAFE);
+                        if (j < n_un) steady(j++, I4(), std::false_type(), SAFE);
+                    }
+                }
+            }
+            // masked steps up to n_kt - 2
+            for (; j <= n_kt - 2; ++j) masked(j, SAFE);
+            // last tile jl: no copy in flight, no product S(jl+1); then its own PV
+            {
+                const int jl = n_kt - 1;
+                wait_vm_lgkm0<0>();
+                refresh_lane();
+                asm volatile("" : "+v"(k_off));
+                asm volatile("" : "+v"(v_off));
+                u32x4_t kf_unused[NKS];
+                f32x16_t s_unused[2];
+                if (jl > 0) read_v(stage_of(jl - 1));
+                if (kt0 + jl >= n_full)
+                    compute(kt0 + jl, std::false_type(), std::true_type(), std::true_type(),
+                            SAFE, kf_unused, s_unused, 0, ring<D, 0>());
+                else
+                    compute(kt0 + jl, std::false_type(), std::true_type(), std::false_type(),
+                            SAFE, kf_unused, s_unused, 0, ring<D, 0>());
+                read_v(stage_of(jl));
+                pv_last();
+            }
         }
-        // masked steps up to n_kt - 2
-        for (; j <= n_kt - 2; ++j) masked(j);
-        // last tile jl: no copy in flight, no product S(jl+1); then its own PV
-        {
-            const int jl = n_kt - 1;
-            wait_vm_lgkm0<0>();
-            refresh_lane();
-            asm volatile("" : "+v"(k_off));
-            asm volatile("" : "+v"(v_off));
-            u32x4_t kf_unused[NKS];
-            f32x16_t s_unused[2];
-            if (jl > 0) read_v(stage_of(jl - 1));
-            if (kt0 + jl >= n_full)
-                compute(kt0 + jl, std::false_type(), std::true_type(), std::true_type(),
-                        std::false_type(), kf_unused, s_unused, 0, ring<D, 0>());
-            else
-                compute(kt0 + jl, std::false_type(), std::true_type(), std::false_type(),
-                        std::false_type(), kf_unused, s_unused, 0, ring<D, 0>());
-            read_v(stage_of(jl));
-            pv_last();
-        }
-    }
+    };
+    run_keys(std::false_type());
 
     // Merge of the KQ waves that share a row half.  Every wave stores its
     // (m, l, lr) and accumulators, relative to its own reference max, in
@@ -817,8 +840,6 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     //   m = max_q m_q,  x = sum_q x_q 2^(m_q - m).
     constexpr int SPS = L::SLOTS_PER_STAGE;
     constexpr int BPW = 2 * NDB / KQ;    // output blocks per wave
-    __syncthreads();                     // every wave is done with the ring
-    refresh_lane();
     auto slot_acc = [&](int w) {
         lds16_t* base = ring<D, 0>();
         const int si = w / SPS;
@@ -831,7 +852,16 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         return reinterpret_cast<lds_f32_t*>(ring<D, STAGES - 1>()) +
                ((w * 2 + rb) * 3 + k) * 64;
     };
-    {
+    // overflow flag of wave w: a word near the end of the statistics' stage
+    auto ovf_flag = [&](int w) {
+        return reinterpret_cast<lds_f32_t*>(ring<D, STAGES - 1>()) + (L::STAGE / 2 - 2 - w);
+    };
+    static_assert(L::WAVES * 2 * 3 * 64 + L::WAVES + 1 <= L::STAGE / 2, "flags");
+    // Every wave stores its accumulators and statistics and whether its
+    // short-form sums overflowed (inf or NaN: they only grow).
+    auto publish = [&]() {
+        __syncthreads();                 // every wave is done with the ring
+        refresh_lane();
         lds_f4_t* a = slot_acc(wave);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -846,8 +876,38 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             stat(wave, rb, 1)[lane] = l[rb];
             stat(wave, rb, 2)[lane] = lr[rb];
         }
+        const bool bad = __builtin_amdgcn_ballot_w64(!(lr[0] + lr[1] < __builtin_inff())) != 0;
+        if (lane == 0) *ovf_flag(wave) = bad ? 1.0f : 0.0f;
+        __syncthreads();
+    };
+    publish();
+    bool redo = false;
+#pragma unroll
+    for (int w = 0; w < L::WAVES; ++w) redo |= *ovf_flag(w) != 0.0f;
+    if (redo) {
+        // some probability left its range: the q-tile again in the safe
+        // form (the flags are read before the ring is refilled: the first
+        // copy into their stage follows two barriers of the key loop)
+        refresh_lane();
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            m[rb] = -__builtin_inff();
+            nm[rb] = 0.0f;
+            l[rb] = 0.0f;
+            lr[rb] = 0.0f;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x16_t{};
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) p_prev[rb][c] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) vf[db][c] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+        run_keys(std::true_type());
+        publish();
     }
-    __syncthreads();
 
     // Merged result of output block bi of this row half, relative to mu.
     struct Block {

@@ -299,6 +299,36 @@ def test_dominant_key():
     assert np.max(np.abs(o[0, 0] - want[None])) <= 1e-5
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,boost", [
+    (F16, 1.5),      # up to ~2^11 above the first tile's max: in range
+    (F16, 10.0),     # ~2^30 and more: past fp16, redone in the safe form
+    (BF16, 10.0),    # in bf16 range
+    (BF16, 100.0),   # ~2^300 and more: past fp32, redone in the safe form
+])
+def test_reference_jump(d, causal, dtype, boost):
+    """A key in a late tile scores far above the first tile's maximum.
+
+    The references are set from the first key tile and only an overflow of
+    the probabilities sends a q-tile through the safe form again, so these
+    cases cover both paths against the oracle.
+    """
+    note(f"reference jump d {d} causal {causal} {dtype} boost {boost}")
+    b, h, lq, lk, j_big = 1, 2, 300, 300, 200
+    q, k, v = workloads.make_dense(b, h, h, lq, lk, d, dtype, seed=21)
+    q = q.float()
+    k = k.float()
+    q[..., 0] = q[..., 0].abs() + 2.0           # every row leans on column 0
+    k[:, :, j_big, 0] = boost * math.sqrt(d)    # score q0 * boost, q0 in [2, 5]
+    q, k = q.to(dtype), k.to(dtype)
+    o, lse = run_gpu(q, k, v, causal=causal)
+    o_ref, l_ref = oracle.attention(workloads.to_f64(q), workloads.to_f64(k),
+                                    workloads.to_f64(v), causal=causal)
+    eo, el = compare(o, lse, o_ref, l_ref)
+    note(f"  err_O {eo:.3e}  err_LSE {el:.3e}")
+
+
 def test_permutation_invariance():
     note("permutation invariance")
     q, k, v = workloads.make_dense(1, 2, 2, 130, 250, 64, BF16, seed=11)
