@@ -334,19 +334,42 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         return CAUSAL ? min(lk_b - 1, qrow(rb) + diag) : lk_b - 1;
     };
     u32x4_t qf[2][NKS];
-    // issued in the prologue between the copies of tiles 0 and 1, so that
-    // their latency overlaps the copies' and one wait covers both
+    // The two waves of a row half need the same fragments: each loads the
+    // k-steps of its key group's half (issued in the prologue between the
+    // copies of tiles 0 and 1, so that one wait covers both) and they swap
+    // halves through LDS stage 3, which no copy fills before step 0.
+    constexpr int KH = NKS / 2;          // k-steps loaded per wave
+    // (fragments indexed by constants only, picked by the wave-uniform kq)
     auto load_q = [&]() {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                u32x4_t x = {0u, 0u, 0u, 0u};
-                if (qrow(rb) < lq_b)
-                    x = *reinterpret_cast<const u32x4_t*>(
+                qf[rb][ks] = u32x4_t{0u, 0u, 0u, 0u};
+                if (ks / KH == kq && qrow(rb) < lq_b)
+                    qf[rb][ks] = *reinterpret_cast<const u32x4_t*>(
                         qg + (int64_t)(qrow(rb) - row0) * p.q_sr + ks * 16 + 8 * hi);
-                qf[rb][ks] = x;
             }
+    };
+    // fragment (rh, rb, ks) of the exchange area, 64 lanes x 16 bytes
+    auto q_slot = [&](int rb, int ks) {
+        return reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(ring<D, 3>()) +
+               ((rh * 2 + rb) * NKS + ks) * 64 + lane;
+    };
+    static_assert(2 * 2 * NKS * 64 * 16 <= L::STAGE * 2, "Q exchange area");
+    auto put_q = [&]() {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                if (ks / KH == kq) *q_slot(rb, ks) = qf[rb][ks];
+    };
+    auto get_q = [&]() {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                if (ks / KH != kq) qf[rb][ks] = *q_slot(rb, ks);
     };
 
     // DMA plan of this lane: which block of a tile it fills and the byte
@@ -743,28 +766,33 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     // safe form only when the short form overflowed (see compute).
     auto run_keys = [&](auto SAFE) {
         if (n_kt > 0) {
-            // prologue: tiles 0 .. AHEAD-1 in flight; wait for tile 0 and
-            // compute S(0)
+            // prologue: tiles 0 and 1 in flight, then Q and tile 0 landed;
+            // S(0)
+            // (tile 2 only after the barrier: less traffic in flight while
+            // every work-group waits for its first tile)
             issue_tile(kt0, ring<D, 0>());
             load_q();
             issue_tile(kt0 + 1, ring<D, 1>());
-            issue_tile(kt0 + 2, ring<D, 2>());
             static_assert(AHEAD == 3, "prologue copies");
-            wait_vm<(AHEAD - 1) * DPW>();    // tiles 1 .. AHEAD-1 may be pending
+            wait_vm<DPW>();              // tile 1 may be pending
+            put_q();
+            wait_vm_lgkm0<DPW>();
+            __builtin_amdgcn_s_barrier();
+            issue_tile(kt0 + 2, ring<D, 2>());
+            get_q();
             if (p.negate_q) {                // scale < 0: fold the sign into q
-    #pragma unroll
+#pragma unroll
                 for (int rb = 0; rb < 2; ++rb)
-    #pragma unroll
+#pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] ^= 0x80008000u;
             }
-            __builtin_amdgcn_s_barrier();
             {
                 u32x4_t kf[NKS];
                 read_k(ring<D, 0>(), kf);
-    #pragma unroll
+#pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
                     s_cur[rb] = f32x16_t{};
-    #pragma unroll
+#pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
                         s_cur[rb] = Mma<Tin>::run(kf[ks], qf[rb][ks], s_cur[rb]);
                 }
@@ -772,7 +800,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             // references from the first tile's row maxima (its masked scores
             // excluded); every step then takes the short form of the softmax
             if (kt0 >= n_full) mask_cur(kt0);
-    #pragma unroll
+#pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
                 const f32x16_t& x = s_cur[rb];
                 const float a0 = max2(max2(x[0], x[1]), x[2]);
@@ -1063,6 +1091,12 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 template <int D, typename Tin, typename Tout, bool CAUSAL>
 __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn_fwd_mfma_kernel(
     FwdParams p, int n_qtiles, int pair, SplitOrder so) {
+    // every argument the work-group reads, requested in one round trip
+    // (otherwise the item decode's wait splits them into two)
+    asm volatile("" ::"s"(p.q), "s"(p.k), "s"(p.v), "s"(p.o), "s"(p.lse),
+                 "s"(p.q_sh), "s"(p.k_sh), "s"(p.v_sh), "s"(p.q_sr), "s"(p.k_sr),
+                 "s"(p.v_sr), "s"(p.o_sh), "s"(p.o_sr), "s"(p.lq), "s"(p.lk),
+                 "s"(p.group), "s"(p.scale_log2));
     const int bh_count = p.hq * p.batch;
     const int item = (int)blockIdx.x / bh_count;
     const int bh = (int)blockIdx.x - item * bh_count;
