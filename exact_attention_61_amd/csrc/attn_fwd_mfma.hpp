@@ -265,8 +265,8 @@ __device__ __forceinline__ lds16_t* ring() {
 
 template <int D, typename Tin, typename Tout, bool CAUSAL>
 __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
-                                             int h, int b, int chunk,
-                                             int nchunks, int n_qtiles) {
+                                             int h, int b, int kt_lo, int kt_hi,
+                                             int chunk, int64_t tile_id) {
     using L = Layout<D>;
     constexpr int BN = L::BN, KQ = L::KQ;
     constexpr int NKC = L::NKC, NKS = L::NKS, NDB = L::NDB;
@@ -315,13 +315,14 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                          (packed ? 0 : (int64_t)b * p.v_sb) +
                          (int64_t)g * p.v_sh + (int64_t)k0 * p.v_sr;
 
-    // Key tiles this q-tile needs, and the chunk [kt0, kt1) of them this
-    // work-group takes (all of them unless the q-tile is split).
+    // Key tiles this q-tile needs, and the range [kt0, kt1) of them this
+    // work-group takes: all of them (kt_hi < 0), or one of the two chunks
+    // of a split q-tile (chunk 0 or 1, partial result under tile_id).
     int kend = lk_b;
     if (CAUSAL) kend = min(kend, row0 + kBM + diag);
     const int n_kt_all = kend > 0 ? (kend + BN - 1) / BN : 0;
-    const int kt0 = chunk * n_kt_all / nchunks;
-    const int kt1 = (chunk + 1) * n_kt_all / nchunks;
+    const int kt0 = kt_hi < 0 ? 0 : kt_lo;
+    const int kt1 = kt_hi < 0 ? n_kt_all : min(kt_hi, n_kt_all);
     const int n_kt = kt1 - kt0;          // steps of this work-group
 
     // Q fragments (B operand of S^T = K Q^T) of the wave's two row blocks:
@@ -1005,7 +1006,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     Block blk[BPW];
 #pragma unroll
     for (int i = 0; i < BPW; ++i) blk[i] = combine(kq * BPW + i);
-    if (nchunks == 1) {
+    if (chunk < 0) {
 #pragma unroll
         for (int i = 0; i < BPW; ++i) store(kq * BPW + i, blk[i]);
         return;
@@ -1016,8 +1017,6 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     // resets the counter for the next call.
     constexpr int kMaxChunks = 2;
     constexpr int kFields = 19;          // o[16], mu, lf, lrf
-    const int64_t tile_id = ((int64_t)b * p.hq + h) * p.split_tiles +
-                            (n_qtiles - 1 - qtile);   // split q-tiles only
     auto part = [&](int c, int bi, int k) {   // chunk, row half, block, field
         return p.split_ws +
                ((((tile_id * kMaxChunks + c) * 2 + rh) * (2 * NDB) + bi) * kFields + k) *
@@ -1051,7 +1050,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         const int before = __hip_atomic_fetch_add(p.split_cnt + tile_id, 1,
                                                   __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
-        *flag = before == nchunks - 1 ? 1.0f : 0.0f;
+        *flag = before == kMaxChunks - 1 ? 1.0f : 0.0f;
     }
     __syncthreads();
     if (*flag == 0.0f) return;           // the other chunk finishes the q-tile
@@ -1083,14 +1082,41 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Key tiles of q-tile t of a dense causal input.
+template <int D>
+__device__ __host__ inline int causal_key_tiles(const FwdParams& p, int t) {
+    const int64_t kend = std::min<int64_t>(p.lk, (int64_t)(t + 1) * kBM + p.lk - p.lq);
+    return kend > 0 ? (int)((kend + Layout<D>::BN - 1) / Layout<D>::BN) : 0;
+}
+
+// Split point of causal pair i (q-tiles h = n-1-i and l = i, n q-tiles): the
+// first x key tiles of h form one item, q-tile l and the rest of h the
+// other, so both take about (tiles(h) + tiles(l) + extra) / 2 steps, extra
+// being the cost of the second item's second q-tile in steps.  x = tiles(h)
+// (no split) when l alone is already that long.
+template <int D>
+__device__ __host__ inline int causal_pair_split(const FwdParams& p, int n, int i) {
+    const int th = causal_key_tiles<D>(p, n - 1 - i);
+    const int tl = causal_key_tiles<D>(p, i);
+    const int x = (th + tl + p.pair_extra + 1) / 2;
+    return x < (th + 1) / 2 ? (th + 1) / 2 : x > th ? th : x;
+}
+
 // Grid: blockIdx.x = item * (hq * batch) + (batch, head) index, so that
-// consecutive work-groups take the same item of different heads.  Items are
-// q-tiles, heaviest first for causal inputs.  With `pair` (causal only) item t
-// covers q-tiles n-1-t and t, which together see n+1 key tiles; the middle
-// tile of an odd count runs alone.
+// consecutive work-groups take the same item of different heads.
+//   non-causal: item = q-tile.
+//   causal, pair_split (dense inputs): items 2i and 2i+1 share the work of
+//     q-tiles n-1-i and i (see causal_pair_split); item 2i takes the first
+//     x key tiles of q-tile n-1-i, item 2i+1 q-tile i and then the rest of
+//     q-tile n-1-i; the two partial results of a split q-tile are merged
+//     through the workspace.  The middle q-tile of an odd count is item
+//     n-1, alone.
+//   causal otherwise: q-tiles heaviest first; with `pair` 1 item t covers
+//     q-tiles n-1-t and t; with `pair` 2 the first half of the grid goes
+//     heaviest-first and the second half lightest-first.
 template <int D, typename Tin, typename Tout, bool CAUSAL>
 __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn_fwd_mfma_kernel(
-    FwdParams p, int n_qtiles, int pair, SplitOrder so) {
+    FwdParams p, int n_qtiles, int pair) {
     // every argument the work-group reads, requested in one round trip
     // (otherwise the item decode's wait splits them into two)
     asm volatile("" ::"s"(p.q), "s"(p.k), "s"(p.v), "s"(p.o), "s"(p.lse),
@@ -1102,127 +1128,95 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
     const int bh = (int)blockIdx.x - item * bh_count;
     const int h = bh % p.hq;
     const int b = bh / p.hq;
-    // q-tiles of this work-group (one call site keeps the code compact)
-    int tiles[2] = {item, -1};
-    int chunk = 0, nchunks = 1;
-    if (CAUSAL && p.split_tiles > 0) {
-        // longest item first: the chunks of the split_tiles last q-tiles and
-        // the other q-tiles, in the order the host sorted them
-        const int e = so.e[item];
-        tiles[0] = e >> 1;
-        chunk = e & 1;
-        nchunks = tiles[0] >= n_qtiles - p.split_tiles ? 2 : 1;
+    // up to two parts: q-tile, key range (hi < 0: all), chunk (-1: whole)
+    int tile[2] = {item, -1}, lo[2] = {0, 0}, hi[2] = {-1, -1}, chunk[2] = {-1, -1};
+    int64_t tile_id = 0;
+    if (CAUSAL && p.pair_split) {
+        const int n = n_qtiles;
+        if ((n & 1) && item == n - 1) {
+            tile[0] = n / 2;
+        } else {
+            const int i = item >> 1;
+            const int th = causal_key_tiles<D>(p, n - 1 - i);
+            const int x = causal_pair_split<D>(p, n, i);
+            tile_id = (int64_t)bh * (n / 2) + i;
+            if ((item & 1) == 0) {
+                tile[0] = n - 1 - i;
+                if (x < th) { lo[0] = 0; hi[0] = x; chunk[0] = 0; }
+            } else {
+                tile[0] = i;
+                if (x < th) { tile[1] = n - 1 - i; lo[1] = x; hi[1] = th; chunk[1] = 1; }
+            }
+        }
     } else if (CAUSAL) {
         if (pair == 2) {
-            // first half of the grid heaviest-first, second half
-            // lightest-first: work-groups i and i + grid/2, which the
-            // dispatcher tends to place on the same CU, see n+1 key tiles
             const int half = n_qtiles / 2;
-            tiles[0] = item < half ? n_qtiles - 1 - item : item - half;
+            tile[0] = item < half ? n_qtiles - 1 - item : item - half;
         } else {
-            tiles[0] = n_qtiles - 1 - item;
-            if (pair == 1 && item < tiles[0]) tiles[1] = item;
+            tile[0] = n_qtiles - 1 - item;
+            if (pair == 1 && item < tile[0]) tile[1] = item;
         }
     }
-    for (int it = 0; it < 2 && tiles[it] >= 0; ++it) {
+    for (int it = 0; it < 2 && tile[it] >= 0; ++it) {
         if (it > 0) __syncthreads();     // the LDS stages are reused
-        attend_qtile<D, Tin, Tout, CAUSAL>(p, tiles[it], h, b, chunk, nchunks,
-                                           n_qtiles);
+        attend_qtile<D, Tin, Tout, CAUSAL>(p, tile[it], h, b, lo[it], hi[it],
+                                           chunk[it], tile_id);
     }
 }
 
 template <int D, typename Tin, typename Tout>
-hipError_t launch_typed(const FwdParams& p, const SplitOrder& so,
-                        hipStream_t stream) {
+hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
     const int n_qtiles = (p.lq + kBM - 1) / kBM;
-    // causal q-tile order: with two resident work-groups per CU, grid halves
-    // heaviest-first and lightest-first; with one, q-tile pairs
+    // causal q-tile order without the pair split: with two resident
+    // work-groups per CU, grid halves heaviest-first and lightest-first;
+    // with one, q-tile pairs
     const int pair = !p.causal ? 0
                      : p.causal_pairs >= 0 ? p.causal_pairs
                      : (Layout<D>::WG_PER_CU == 2 ? 2 : 1);
-    const int items = (p.causal && p.split_tiles > 0) ? n_qtiles + p.split_tiles
-                      : pair == 1 ? (n_qtiles + 1) / 2 : n_qtiles;
+    const int items = (p.causal && !p.pair_split && pair == 1) ? (n_qtiles + 1) / 2
+                                                                : n_qtiles;
     const int64_t blocks = (int64_t)items * p.hq * p.batch;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (p.causal)
         hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true>),
                            dim3((unsigned)blocks), dim3(Layout<D>::THREADS), 0,
-                           stream, p, n_qtiles, pair, so);
+                           stream, p, n_qtiles, pair);
     else
         hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, false>),
                            dim3((unsigned)blocks), dim3(Layout<D>::THREADS), 0,
-                           stream, p, n_qtiles, 0, so);
+                           stream, p, n_qtiles, 0);
     return hipGetLastError();
 }
 
-// Causal key-split plan (host): how many of the last q-tiles of every
-// (batch, head) to process as two key chunks, so that no work-group's item is
-// much longer than the average work per resident work-group.  0 = none.
+// Pairs of a causal launch with the pair split whose first q-tile is split
+// (they need a workspace slot), per (batch, head); 0 = the split changes
+// nothing.
 template <int D>
-int split_tiles(const FwdParams& p, int cus) {
-    using L = Layout<D>;
+int causal_split_pairs(const FwdParams& p) {
     if (!p.causal || p.cu_q != nullptr || p.lq <= 0 || p.lk <= 0) return 0;
     const int n = (p.lq + kBM - 1) / kBM;
-    auto n_kt = [&](int t) {
-        const int64_t kend = std::min<int64_t>(p.lk, (int64_t)(t + 1) * kBM + p.lk - p.lq);
-        return kend > 0 ? (int)((kend + L::BN - 1) / L::BN) : 0;
-    };
-    int64_t total = 0;
-    for (int t = 0; t < n; ++t) total += n_kt(t);
-    total *= (int64_t)p.batch * p.hq;
-    const double avg = (double)total / ((double)cus * L::WG_PER_CU);
-    const int maxk = n_kt(n - 1);
-    if (maxk < 8 || maxk <= 1.5 * avg) return 0;
-    int hs = 0;
-    while (hs < n && 2 * n_kt(n - 1 - hs) > maxk) ++hs;
-    if (n + hs > SplitOrder::kMaxItems) return 0;
-    return hs;
+    int any = 0;
+    for (int i = 0; i < n / 2; ++i)
+        if (causal_pair_split<D>(p, n, i) < causal_key_tiles<D>(p, n - 1 - i)) any = 1;
+    return any ? n / 2 : 0;
 }
 
-// Items of a split launch sorted longest first (ties: later q-tile first):
-// entry = q-tile * 2 + chunk; the split_tiles last q-tiles have two chunks.
-template <int D>
-void split_order(const FwdParams& p, int hs, SplitOrder& so) {
-    using L = Layout<D>;
-    const int n = (p.lq + kBM - 1) / kBM;
-    auto n_kt = [&](int t) {
-        const int64_t kend = std::min<int64_t>(p.lk, (int64_t)(t + 1) * kBM + p.lk - p.lq);
-        return kend > 0 ? (int)((kend + L::BN - 1) / L::BN) : 0;
-    };
-    struct It { int len, e; };
-    It items[SplitOrder::kMaxItems];
-    int m = 0;
-    for (int t = n - 1; t >= 0; --t) {
-        const int k = n_kt(t);
-        if (t >= n - hs) {
-            items[m++] = {k / 2, 2 * t};           // chunk 0: [0, k/2)
-            items[m++] = {k - k / 2, 2 * t + 1};   // chunk 1: [k/2, k)
-        } else {
-            items[m++] = {k, 2 * t};
-        }
-    }
-    std::stable_sort(items, items + m,
-                     [](const It& a, const It& b) { return a.len > b.len; });
-    for (int i = 0; i < m; ++i) so.e[i] = (uint16_t)items[i].e;
-}
-
-// Workspace of a key-split launch: floats per split q-tile, in the order of
-// the kernel's partial results (2 chunks x 2 row halves x output blocks x 19
-// fields x 64 lanes).
+// Workspace floats per split q-tile, in the order of the kernel's partial
+// results (2 chunks x 2 row halves x output blocks x 19 fields x 64 lanes).
 template <int D>
 constexpr int64_t split_floats_per_tile() {
     return 2 * 2 * (2 * Layout<D>::NDB) * 19 * 64;
 }
 
 template <int D>
-hipError_t launch_d(const FwdParams& p, const SplitOrder& so, int in_dtype,
-                    int out_dtype, hipStream_t stream) {
+hipError_t launch_d(const FwdParams& p, int in_dtype, int out_dtype,
+                    hipStream_t stream) {
     if (in_dtype == 0) {
-        return out_dtype == 2 ? launch_typed<D, f16_t, float>(p, so, stream)
-                              : launch_typed<D, f16_t, f16_t>(p, so, stream);
+        return out_dtype == 2 ? launch_typed<D, f16_t, float>(p, stream)
+                              : launch_typed<D, f16_t, f16_t>(p, stream);
     }
-    return out_dtype == 2 ? launch_typed<D, bf16_t, float>(p, so, stream)
-                          : launch_typed<D, bf16_t, bf16_t>(p, so, stream);
+    return out_dtype == 2 ? launch_typed<D, bf16_t, float>(p, stream)
+                          : launch_typed<D, bf16_t, bf16_t>(p, stream);
 }
 
 }  // namespace

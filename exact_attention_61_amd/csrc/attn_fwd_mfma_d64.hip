@@ -3,16 +3,12 @@
 
 namespace mi_attn {
 
-hipError_t launch_mfma_d64(const FwdParams& p, const SplitOrder& so,
-                          int in_dtype, int out_dtype, hipStream_t stream) {
-    return launch_d<64>(p, so, in_dtype, out_dtype, stream);
+hipError_t launch_mfma_d64(const FwdParams& p, int in_dtype, int out_dtype,
+                          hipStream_t stream) {
+    return launch_d<64>(p, in_dtype, out_dtype, stream);
 }
 
-int split_tiles_d64(const FwdParams& p, int cus) { return split_tiles<64>(p, cus); }
-
-void split_order_d64(const FwdParams& p, int hs, SplitOrder& so) {
-    split_order<64>(p, hs, so);
-}
+int causal_split_pairs_d64(const FwdParams& p) { return causal_split_pairs<64>(p); }
 
 int64_t split_floats_per_tile_d64() { return split_floats_per_tile<64>(); }
 

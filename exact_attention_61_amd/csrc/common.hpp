@@ -27,21 +27,16 @@ struct FwdParams {
     int32_t negate_q;                // 1 when scale < 0 (fold the sign into q)
     int32_t causal;
     int32_t causal_pairs;            // causal q-tile order (0, 1, 2; -1 default)
-    // Key-split of heavy causal q-tiles: the split_tiles last q-tiles of
-    // every (batch, head) are processed as two key chunks by two work-groups;
-    // the later one merges the other's partial result from split_ws (indexed
-    // by (batch, head, q-tile, chunk)) and resets the q-tile's counter in
-    // split_cnt.  0 = no split (split_ws, split_cnt unused).
-    int32_t split_tiles;
+    // Pair split of dense causal inputs: q-tiles n-1-i and i are shared by
+    // two work-groups of about equal length; a q-tile split between them
+    // leaves two partial results in split_ws (indexed by (batch, head,
+    // pair)) and the later work-group merges them and resets the pair's
+    // counter in split_cnt.  pair_extra: the second q-tile's fixed cost in
+    // key tiles.  0 = off (split_ws, split_cnt unused).
+    int32_t pair_split;
+    int32_t pair_extra;
     float* split_ws;
     int32_t* split_cnt;
-};
-
-// Item order of a split launch, longest first: entry = q-tile * 2 + chunk.
-// A kernel argument of its own, read only by the work-group's item decode.
-struct SplitOrder {
-    static constexpr int kMaxItems = 256;
-    uint16_t e[kMaxItems];
 };
 
 // Storage tags for the element types (16-bit values are kept as raw bits).
@@ -90,17 +85,16 @@ template <> struct OutStore<float> {
 // argument was validated by the caller.  Return the hipGetLastError() code.
 hipError_t launch_simple(const FwdParams& p, int in_dtype, int out_dtype,
                          int head_dim, hipStream_t stream);
-hipError_t launch_mfma_d64(const FwdParams& p, const SplitOrder& so,
-                          int in_dtype, int out_dtype, hipStream_t stream);
-hipError_t launch_mfma_d128(const FwdParams& p, const SplitOrder& so,
-                           int in_dtype, int out_dtype, hipStream_t stream);
-// Key-split plan of the MFMA kernel (q-tiles to split per (batch, head)) and
-// the workspace floats each split q-tile needs.
-int split_tiles_d64(const FwdParams& p, int cus);
-int split_tiles_d128(const FwdParams& p, int cus);
+hipError_t launch_mfma_d64(const FwdParams& p, int in_dtype, int out_dtype,
+                          hipStream_t stream);
+hipError_t launch_mfma_d128(const FwdParams& p, int in_dtype, int out_dtype,
+                           hipStream_t stream);
+// Pair split of the MFMA kernel: pairs per (batch, head) that need a
+// workspace slot (0: the split changes nothing) and the workspace floats
+// per slot.
+int causal_split_pairs_d64(const FwdParams& p);
+int causal_split_pairs_d128(const FwdParams& p);
 int64_t split_floats_per_tile_d64();
-void split_order_d64(const FwdParams& p, int hs, SplitOrder& so);
-void split_order_d128(const FwdParams& p, int hs, SplitOrder& so);
 int64_t split_floats_per_tile_d128();
 
 }  // namespace mi_attn

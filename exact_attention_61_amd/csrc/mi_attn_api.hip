@@ -56,29 +56,24 @@ int causal_pairs_setting() {
     return v;
 }
 
-// MI_ATTN_SPLIT=1 turns on the key-split of heavy causal q-tiles (read on
-// every call).  Off by default: at the sizes measured so far the extra
-// work-groups' fixed cost outweighs the better balance.
+// Pair split of dense causal inputs (see FwdParams): MI_ATTN_SPLIT=1 turns
+// it on (read on every call).  Off by default: at the sizes measured so far
+// the second q-tile's fixed cost and the hand-over of the partial results
+// outweigh the better balance.  MI_ATTN_PAIR_EXTRA overrides the second
+// q-tile's fixed cost in key tiles (default 4).
 bool split_enabled() {
     const char* e = std::getenv("MI_ATTN_SPLIT");
     return e != nullptr && std::strcmp(e, "1") == 0;
 }
 
-int cu_count(int dev) {
-    static std::mutex mu;
-    static std::map<int, int> cache;
-    std::lock_guard<std::mutex> lock(mu);
-    auto it = cache.find(dev);
-    if (it != cache.end()) return it->second;
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-            hipSuccess || cus <= 0)
-        cus = 256;
-    cache[dev] = cus;
-    return cus;
+int pair_extra_setting() {
+    const char* e = std::getenv("MI_ATTN_PAIR_EXTRA");
+    if (e == nullptr) return 4;
+    const int x = std::atoi(e);
+    return x >= 0 && x <= 64 ? x : 4;
 }
 
-// Workspace of the causal key-split, one per device, in kSplitRegions
+// Workspace of the causal pair split, one per device, in kSplitRegions
 // regions used in turn, one per call: calls in flight at once (several
 // streams, or one graph's launches) use different regions as long as at most
 // kSplitRegions of them overlap.  A region's counters are back at zero when
@@ -219,33 +214,26 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
     p.causal_pairs = causal_pairs_setting();
 
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    p.split_tiles = 0;
-    mi_attn::SplitOrder so{};
+    p.pair_split = 0;
+    p.pair_extra = pair_extra_setting();
+    p.split_ws = nullptr;
+    p.split_cnt = nullptr;
     if (!use_scalar_kernel() && split_enabled() && causal && !packed) {
-        int dev = 0;
-        if (hipGetDevice(&dev) == hipSuccess) {
-            const int cus = cu_count(dev);
-            const int hs = head_dim == 64 ? mi_attn::split_tiles_d64(p, cus)
-                                          : mi_attn::split_tiles_d128(p, cus);
-            const int64_t per = head_dim == 64 ? mi_attn::split_floats_per_tile_d64()
-                                               : mi_attn::split_floats_per_tile_d128();
-            const int64_t tiles = (int64_t)batch * hq * hs;
-            if (hs > 0 && split_workspace(st, tiles * per, tiles, &p.split_ws,
-                                          &p.split_cnt)) {
-                p.split_tiles = hs;
-                if (head_dim == 64) mi_attn::split_order_d64(p, hs, so);
-                else mi_attn::split_order_d128(p, hs, so);
-            }
-        }
+        const int np = head_dim == 64 ? mi_attn::causal_split_pairs_d64(p)
+                                      : mi_attn::causal_split_pairs_d128(p);
+        const int64_t per = head_dim == 64 ? mi_attn::split_floats_per_tile_d64()
+                                           : mi_attn::split_floats_per_tile_d128();
+        const int64_t slots = (int64_t)batch * hq * np;
+        if (np > 0 && split_workspace(st, slots * per, slots, &p.split_ws, &p.split_cnt))
+            p.pair_split = 1;
     }
     const hipError_t err =
         use_scalar_kernel()
             ? mi_attn::launch_simple(p, (int)in_dtype, (int)out_dtype,
                                      head_dim, st)
             : head_dim == 64
-                  ? mi_attn::launch_mfma_d64(p, so, (int)in_dtype, (int)out_dtype, st)
-                  : mi_attn::launch_mfma_d128(p, so, (int)in_dtype, (int)out_dtype,
-                                              st);
+                  ? mi_attn::launch_mfma_d64(p, (int)in_dtype, (int)out_dtype, st)
+                  : mi_attn::launch_mfma_d128(p, (int)in_dtype, (int)out_dtype, st);
     if (err != hipSuccess) {
         g_last_hip_error = (int32_t)err;
         return MI_ATTN_ERR_HIP;

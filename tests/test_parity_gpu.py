@@ -349,28 +349,44 @@ def test_repeat_runs_are_bit_identical():
 
 
 # ---------------------------------------------------------------------------
-# Key-split of heavy causal q-tiles (MI_ATTN_SPLIT=1): two work-groups take
-# the two key halves of each heavy q-tile and the later one merges the
-# other's partial result.  Head counts that are not multiples of 8 put the
+# Pair split of dense causal inputs (MI_ATTN_SPLIT=1): q-tiles n-1-i and i are
+# shared by two work-groups; the heavy q-tile's first key tiles go to one,
+# the light q-tile and the rest of the heavy one to the other, and the later
+# of the two merges the heavy q-tile's partial results.  MI_ATTN_PAIR_EXTRA
+# moves the split point; head counts that are not multiples of 8 put the
 # two halves on different XCDs, so the hand-over is checked across them.
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("extra", ["0", "4", "16"])
 @pytest.mark.parametrize("b,h,lq,lk,d,dtype", [
     (1, 3, 1024, 1024, 64, F16),
     (2, 5, 1024, 1024, 64, BF16),
     (1, 5, 1024, 1024, 128, BF16),
-    (1, 3, 700, 1100, 64, F16),
+    (1, 3, 700, 1100, 64, F16),      # more keys than queries
+    (1, 2, 1100, 700, 64, BF16),     # fewer keys: early rows see none
+    (1, 2, 1152, 1152, 64, F16),     # odd q-tile count: the middle one alone
     (1, 2, 2048, 2048, 128, F16),
 ])
-def test_key_split_causal(monkeypatch, b, h, lq, lk, d, dtype):
+def test_pair_split_causal(monkeypatch, extra, b, h, lq, lk, d, dtype):
     monkeypatch.setenv("MI_ATTN_SPLIT", "1")
-    note(f"key split b{b} h{h} lq{lq} lk{lk} d{d} {dtype}")
+    monkeypatch.setenv("MI_ATTN_PAIR_EXTRA", extra)
+    note(f"pair split extra {extra} b{b} h{h} lq{lq} lk{lk} d{d} {dtype}")
     dense_case(b, h, h, lq, lk, d, dtype, True)
 
 
-def test_key_split_repeat_runs_are_bit_identical(monkeypatch):
+@pytest.mark.parametrize("b,h,lq,lk,d,dtype", [
+    (1, 3, 1024, 1024, 64, F16),
+    (1, 3, 700, 1100, 128, BF16),
+])
+def test_causal_without_pair_split(monkeypatch, b, h, lq, lk, d, dtype):
+    monkeypatch.setenv("MI_ATTN_SPLIT", "0")
+    note(f"no pair split b{b} h{h} lq{lq} lk{lk} d{d} {dtype}")
+    dense_case(b, h, h, lq, lk, d, dtype, True)
+
+
+def test_pair_split_repeat_runs_are_bit_identical(monkeypatch):
     monkeypatch.setenv("MI_ATTN_SPLIT", "1")
-    note("key split determinism")
+    note("pair split determinism")
     inp = workloads.make("causal_b2h16", seed=1)
     o1, l1 = run_gpu(inp["q"], inp["k"], inp["v"], causal=True, scale=0.125)
     o2, l2 = run_gpu(inp["q"], inp["k"], inp["v"], causal=True, scale=0.125)
