@@ -527,26 +527,38 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     // and rescale (the accumulators after this step's products).
     auto compute = [&](int j, auto NEXT, auto PV, auto MASK, auto SAFE,
                        const u32x4_t (&kf)[NKS], f32x16_t (&s_next)[2],
-                       int dma_kt, lds16_t* dma_stage) {
+                       int dma_kt, lds16_t* dma_stage, const lds16_t* v_next) {
         constexpr bool next = decltype(NEXT)::value;
         constexpr bool safe = decltype(SAFE)::value;
         constexpr int NPV = decltype(PV)::value ? 2 * NDB * 2 : 0;
         constexpr int NQK = next ? 2 * NKS : 0;
         constexpr int NM = NPV + NQK;
-        constexpr int PV0 = NQK / 2;     // first PV product
         constexpr int kGroups = safe ? 13 : 9;
+        // O += P(j-1) V(j-1) first: its fragments were read in the previous
+        // step.  S(j+1) = Q K(j+1)^T after it, by when the K(j+1) fragments
+        // read at the start of this step have landed.
         auto mfma = [&](int q) {
-            if (q >= PV0 && q < PV0 + NPV) {
-                const int qp = q - PV0;
-                const int c = qp / (2 * NDB), r2 = qp % (2 * NDB);
+            if (q < NPV) {
+                const int c = q / (2 * NDB), r2 = q % (2 * NDB);
                 const int db = r2 / 2, rb2 = r2 % 2;
                 acc[rb2][db] = Mma<Tin>::run(vf[db][c], p_prev[rb2][c], acc[rb2][db]);
             } else if (next) {
-                const int qq = q < PV0 ? q : q - NPV;
-                const int rb2 = qq / NKS, ks = qq % NKS;
+                // row blocks alternate: neighbouring products are independent
+                const int qq = q - NPV;
+                const int rb2 = qq & 1, ks = qq >> 1;
                 s_next[rb2] = Mma<Tin>::run(kf[ks], qf[rb2][ks],
                                             ks == 0 ? f32x16_t{} : s_next[rb2]);
             }
+        };
+        // V(j) for the next step's product, read into vf in the group after
+        // the one that issues the last product reading vf
+        constexpr int kGroupV = [] {
+            int g = 0;
+            while (NPV > 0 && (g + 1) * NM / kGroups < NPV) ++g;
+            return NPV > 0 ? g + 1 : 0;
+        }();
+        auto vread_at = [&](int gi) {
+            if (gi == kGroupV) read_v(v_next);
         };
         if constexpr (decltype(MASK)::value) mask_cur(j);
         u32x4_t p_new[2][2];             // this tile's P; p_prev stays for PV
@@ -568,6 +580,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             float pe[2][4];              // probabilities of the last two parts
 #pragma unroll
             for (int gi = 0; gi < kGroups; ++gi) {
+                vread_at(gi);
                 if (gi < 8) {
                     const int rb = gi >> 2, e0 = 4 * (gi & 3);
                     float* x = pe[gi & 1];
@@ -598,6 +611,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 dma_at(gi, rsrc);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (kGroupV >= kGroups) read_v(v_next);
         } else {
             float psum[2][4];
             float rsr[2][2];             // row sums of the rounded P, per chunk
@@ -605,6 +619,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             float alpha[2] = {1.0f, 1.0f};
 #pragma unroll
             for (int gi = 0; gi < kGroups; ++gi) {
+                vread_at(gi);
                 if (gi == 0) {
                     // lane maxima of both row blocks; rare reference update
                     float mt[2];
@@ -671,6 +686,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 dma_at(gi, rsrc);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (kGroupV >= kGroups) read_v(v_next);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
                 if (Mma<Tin>::kFp32Sum)
@@ -739,11 +755,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         asm volatile("" : "+v"(v_off));
         u32x4_t kf[NKS];
         read_k(ring<D, (S + 1) % STAGES>(), kf);
-        if constexpr (!first) read_v(ring<D, (S + STAGES - 1) % STAGES>());
         f32x16_t s_new[2];
         compute(kt0 + j, std::true_type(), std::integral_constant<bool, !first>(),
                 std::false_type(), SAFE, kf, s_new, kt0 + j + AHEAD,
-                ring<D, (S + AHEAD) % STAGES>());
+                ring<D, (S + AHEAD) % STAGES>(), ring<D, S>());
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s_cur[rb] = s_new[rb];
     };
@@ -755,10 +770,9 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         asm volatile("" : "+v"(v_off));
         u32x4_t kf[NKS];
         read_k(stage_of(j + 1), kf);
-        if (j > 0) read_v(stage_of(j - 1));   // else P(j-1) = 0 and V = 0
-        f32x16_t s_new[2];
+        f32x16_t s_new[2];               // (j = 0: P(j-1) = 0 and V = 0)
         compute(kt0 + j, std::true_type(), std::true_type(), std::true_type(), SAFE,
-                kf, s_new, kt0 + j + AHEAD, stage_of(j + AHEAD));
+                kf, s_new, kt0 + j + AHEAD, stage_of(j + AHEAD), stage_of(j));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s_cur[rb] = s_new[rb];
     };
@@ -848,14 +862,14 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 asm volatile("" : "+v"(v_off));
                 u32x4_t kf_unused[NKS];
                 f32x16_t s_unused[2];
-                if (jl > 0) read_v(stage_of(jl - 1));
+                // vf holds V(jl-1) (zeros if jl = 0); compute reads V(jl)
+                const lds16_t* cur = stage_of(jl);
                 if (kt0 + jl >= n_full)
                     compute(kt0 + jl, std::false_type(), std::true_type(), std::true_type(),
-                            SAFE, kf_unused, s_unused, 0, ring<D, 0>());
+                            SAFE, kf_unused, s_unused, 0, ring<D, 0>(), cur);
                 else
                     compute(kt0 + jl, std::false_type(), std::true_type(), std::false_type(),
-                            SAFE, kf_unused, s_unused, 0, ring<D, 0>());
-                read_v(stage_of(jl));
+                            SAFE, kf_unused, s_unused, 0, ring<D, 0>(), cur);
                 pv_last();
             }
         }
