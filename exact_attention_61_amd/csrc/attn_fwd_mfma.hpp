@@ -148,11 +148,20 @@ template <> struct Mma<bf16_t> {
     }
 };
 
+// Lane index 0..63 from the execution mask (all lanes active), computed anew
+// at every call: the asm is volatile, so the optimiser neither merges two
+// calls nor keeps one result alive across a loop.
+__device__ __forceinline__ int lane_id() {
+    int x;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+    return x;
+}
+
 // Value of x held by lane l ^ 32.
 __device__ __forceinline__ float partner(float x) {
     const uint32_t u = __builtin_bit_cast(uint32_t, x);
     auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    const uint32_t y = (threadIdx.x & 32) ? r[0] : r[1];
+    const uint32_t y = (lane_id() & 32) ? r[0] : r[1];
     return __builtin_bit_cast(float, y);
 }
 
@@ -280,17 +289,20 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     using I3 = std::integral_constant<int, 3>;
     using I4 = std::integral_constant<int, 4>;
 
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // scalar
     const int kq = wave >> 1;            // key group of every tile
     const int rh = wave & 1;             // row half of the q-tile
-    // Lane indices.  Re-pinned (refresh_lane) where the code after the key
-    // loop starts, so offsets derived from them are recomputed there rather
-    // than kept in registers across the loop.
-    int lane = tid & 63;
+    // Lane indices.  Derived afresh (refresh_lane) where the code after the
+    // key loop starts, from the execution mask rather than the thread id, so
+    // nothing derived from the lane stays live (or spilled) across the loop.
+    int lane = lane_id();
     int hi = lane >> 5;                  // which half of the wave
     int col = lane & 31;                 // the query row this lane owns
-    auto refresh_lane = [&]() { asm volatile("" : "+v"(lane), "+v"(hi), "+v"(col)); };
+    auto refresh_lane = [&]() {
+        lane = lane_id();
+        hi = lane >> 5;
+        col = lane & 31;
+    };
 
     int q0 = 0, lq_b = p.lq, k0 = 0, lk_b = p.lk;
     const bool packed = p.cu_q != nullptr;
@@ -1060,7 +1072,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     __syncthreads();
     lds_f32_t* flag = reinterpret_cast<lds_f32_t*>(ring<D, STAGES - 1>()) +
                       (L::STAGE / 2 - 1);   // last word of the stage
-    if (tid == 0) {
+    if (wave == 0 && lane == 0) {
         const int before = __hip_atomic_fetch_add(p.split_cnt + tile_id, 1,
                                                   __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
@@ -1091,7 +1103,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         for (int k = 0; k < 16; ++k) r.o[k] = a.o[k] * fa + c.o[k] * fc;
         store(bi, r);
     }
-    if (tid == 0)                        // ready for the next call
+    if (wave == 0 && lane == 0)          // ready for the next call
         __hip_atomic_store(p.split_cnt + tile_id, 0, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
