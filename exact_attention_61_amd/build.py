@@ -1,6 +1,7 @@
 """Build libmi_attn.so in-tree with hipcc for gfx950.
 
-Usage: python -m exact_attention_61_amd.build   (or build() from Python).
+Usage: python exact_attention_61_amd/build.py   (or build() from Python; the
+file is run directly because importing the package needs the built library).
 Every .hip file under csrc/ is compiled to an object in _build/ and linked
 into exact_attention_61_amd/libmi_attn.so.  It always recompiles.
 """
