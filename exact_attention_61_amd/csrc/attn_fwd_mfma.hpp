@@ -347,42 +347,48 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         return CAUSAL ? min(lk_b - 1, qrow(rb) + diag) : lk_b - 1;
     };
     u32x4_t qf[2][NKS];
-    // The two waves of a row half need the same fragments: each loads the
-    // k-steps of its key group's half (issued in the prologue between the
-    // copies of tiles 0 and 1, so that one wait covers both) and they swap
-    // halves through LDS stage 3, which no copy fills before step 0.
-    constexpr int KH = NKS / 2;          // k-steps loaded per wave
-    // (fragments indexed by constants only, picked by the wave-uniform kq)
-    auto load_q = [&]() {
+    // Q goes to LDS stage 3 (which no K/V copy fills before step 0) by the
+    // same kind of copy as the K/V tiles, in fragment order: block
+    // qb = (rh * 2 + rb) * NKS + ks holds lane l's 8 elements of row
+    // 64 rh + 32 rb + (l & 31) of the q-tile, columns ks*16 + 8*(l >> 5)
+    // .. +7.  Each wave copies NKS of the 4 * NKS blocks; after the first
+    // barrier every wave reads the 2 * NKS blocks of its row half.  Rows
+    // past the sequence end read as zeros (range of the buffer resource).
+    constexpr int QPW = NKS;             // Q blocks copied per wave
+    static_assert(4 * NKS * 512 <= L::STAGE, "Q area fits a stage");
+    auto issue_q = [&]() {
+        const int rows = min(lq_b - row0, kBM);
+        const uint64_t a = reinterpret_cast<uint64_t>(qg);
+        u32x4_t rs;
+        rs[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+        rs[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+        rs[2] = __builtin_amdgcn_readfirstlane((uint32_t)(rows * p.q_sr * 2));
+        rs[3] = 0x00020000u;
+        const int qb0 = wave * QPW;
+        const uint32_t off0 = (uint32_t)((((64 * (qb0 / (2 * NKS)) + 32 * ((qb0 / NKS) & 1) +
+                                             (lane & 31)) * p.q_sr) +
+                                           (qb0 % NKS) * 16 + 8 * (lane >> 5)) * 2);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                qf[rb][ks] = u32x4_t{0u, 0u, 0u, 0u};
-                if (ks / KH == kq && qrow(rb) < lq_b)
-                    qf[rb][ks] = *reinterpret_cast<const u32x4_t*>(
-                        qg + (int64_t)(qrow(rb) - row0) * p.q_sr + ks * 16 + 8 * hi);
-            }
+        for (int t = 0; t < QPW; ++t) {
+            const int qb = qb0 + t;
+            const int drow = 64 * (qb / (2 * NKS) - qb0 / (2 * NKS)) +
+                             32 * (((qb / NKS) & 1) - ((qb0 / NKS) & 1));
+            const int dcol = 16 * (qb % NKS - qb0 % NKS);
+            const uint32_t delta = __builtin_amdgcn_readfirstlane(
+                (uint32_t)((drow * p.q_sr + dcol) * 2));
+            const uint32_t lds_addr =
+                (uint32_t)reinterpret_cast<uintptr_t>(ring<D, 3>() + qb * 512);
+            asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :: "v"(off0 + delta), "s"(rs), "{m0}"(lds_addr) : "memory");
+        }
     };
-    // fragment (rh, rb, ks) of the exchange area, 64 lanes x 16 bytes
-    auto q_slot = [&](int rb, int ks) {
-        return reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(ring<D, 3>()) +
-               ((rh * 2 + rb) * NKS + ks) * 64 + lane;
-    };
-    static_assert(2 * 2 * NKS * 64 * 16 <= L::STAGE * 2, "Q exchange area");
-    auto put_q = [&]() {
+    auto read_q = [&]() {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                if (ks / KH == kq) *q_slot(rb, ks) = qf[rb][ks];
-    };
-    auto get_q = [&]() {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                if (ks / KH != kq) qf[rb][ks] = *q_slot(rb, ks);
+                qf[rb][ks] = *reinterpret_cast<lds_u32x4_t*>(
+                    ring<D, 3>() + ((rh * 2 + rb) * NKS + ks) * 512 + lane * 8);
     };
 
     // DMA plan of this lane: which block of a tile it fills and the byte
@@ -423,17 +429,29 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     // Tiles past the last one get an empty range: their copies read nothing
     // and write zeros, so every step issues the same copies and waits for
     // the same counts.
+    // Buffer resource: base address (48 bits, stride 0), range in bytes, and
+    // the fourth word of a raw 32-bit buffer.
     auto tile_rsrc = [&](int kt) {
         const int rows = kt < kt1 ? min(lk_b - kt * BN, BN) : 0;
-        const int bytes = __builtin_amdgcn_readfirstlane((int)(rows * dma_sr * 2));
-        return __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(dma_base + (int64_t)kt * BN * dma_sr), (short)0, bytes,
-            0x00020000);
+        const uint64_t a = reinterpret_cast<uint64_t>(dma_base + (int64_t)kt * BN * dma_sr);
+        u32x4_t r;
+        r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+        r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+        r[2] = __builtin_amdgcn_readfirstlane((uint32_t)(rows * dma_sr * 2));
+        r[3] = 0x00020000u;
+        return r;
     };
-    auto issue_part = [&](auto rsrc, lds16_t* stage, int t) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc, (__attribute__((address_space(3))) void*)(stage + dma_dst[t]), 16,
-            dma_voff0 + (uint32_t)dma_delta[t], 0, 0, 0);
+    // The copy is written as inline asm (no result register; M0 takes the
+    // LDS address), so the compiler does not track it: every read of a
+    // stage is ordered after the copies into it by this kernel's own vmcnt
+    // waits and the barrier that follows them -- needed anyway, since a
+    // stage is filled by all waves -- and the compiler adds no wait for all
+    // copies in flight where it cannot tell the stages apart.
+    auto issue_part = [&](const u32x4_t& rsrc, lds16_t* stage, int t) {
+        const uint32_t lds_addr = (uint32_t)reinterpret_cast<uintptr_t>(stage + dma_dst[t]);
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :: "v"(dma_voff0 + (uint32_t)dma_delta[t]), "s"(rsrc), "{m0}"(lds_addr)
+                     : "memory");
     };
     auto issue_tile = [&](int kt, lds16_t* stage) {
         const auto rsrc = tile_rsrc(kt);
@@ -542,6 +560,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                        int dma_kt, lds16_t* dma_stage, const lds16_t* v_next) {
         constexpr bool next = decltype(NEXT)::value;
         constexpr bool safe = decltype(SAFE)::value;
+        // Masked steps issue no copy: a q-tile has at most 3 key tiles with
+        // masked keys, all at the end of its range, so the tile a masked step
+        // would fetch (AHEAD = 3 ahead) is always past the range.
+        constexpr bool copy = next && !decltype(MASK)::value;
         constexpr int NPV = decltype(PV)::value ? 2 * NDB * 2 : 0;
         constexpr int NQK = next ? 2 * NKS : 0;
         constexpr int NM = NPV + NQK;
@@ -574,11 +596,11 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         };
         if constexpr (decltype(MASK)::value) mask_cur(j);
         u32x4_t p_new[2][2];             // this tile's P; p_prev stays for PV
-        // The copy of tile dma_kt (NEXT only), one instruction every few
+        // The copy of tile dma_kt (steady steps only), one instruction every few
         // groups: a burst of copies from every wave at once fills the memory
         // pipeline's queue and stalls the waves behind it.
-        auto dma_at = [&](int gi, auto rsrc) {
-            if (next) {
+        auto dma_at = [&](int gi, const u32x4_t& rsrc) {
+            if (copy) {
 #pragma unroll
                 for (int t = 0; t < DPW; ++t)
                     if (gi == 1 + t * (kGroups - 2) / DPW) issue_part(rsrc, dma_stage, t);
@@ -774,8 +796,11 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s_cur[rb] = s_new[rb];
     };
-    auto masked = [&](int j, auto SAFE) {
-        wait_vm<(AHEAD - 2) * DPW>();
+    // Masked steps issue no copies: after the first of them, tile j+1 is the
+    // last copy issued, so the wait is for all of them.
+    auto masked = [&](int j, bool after_copy, auto SAFE) {
+        if (after_copy) wait_vm<(AHEAD - 2) * DPW>();
+        else wait_vm<0>();
         __builtin_amdgcn_s_barrier();
         refresh_lane();
         asm volatile("" : "+v"(k_off));
@@ -793,20 +818,18 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     // safe form only when the short form overflowed (see compute).
     auto run_keys = [&](auto SAFE) {
         if (n_kt > 0) {
-            // prologue: tiles 0 and 1 in flight, then Q and tile 0 landed;
-            // S(0)
+            // prologue: copies of tile 0, Q and tile 1 in flight, then Q
+            // and tile 0 landed; S(0)
             // (tile 2 only after the barrier: less traffic in flight while
             // every work-group waits for its first tile)
             issue_tile(kt0, ring<D, 0>());
-            load_q();
+            issue_q();
             issue_tile(kt0 + 1, ring<D, 1>());
             static_assert(AHEAD == 3, "prologue copies");
-            wait_vm<DPW>();              // tile 1 may be pending
-            put_q();
-            wait_vm_lgkm0<DPW>();
+            wait_vm<DPW>();              // tile 0 and Q in; tile 1 may be pending
             __builtin_amdgcn_s_barrier();
             issue_tile(kt0 + 2, ring<D, 2>());
-            get_q();
+            read_q();
             if (p.negate_q) {                // scale < 0: fold the sign into q
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb)
@@ -863,8 +886,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                     }
                 }
             }
-            // masked steps up to n_kt - 2
-            for (; j <= n_kt - 2; ++j) masked(j, SAFE);
+            // masked steps up to n_kt - 2 (the first follows a step, or the
+            // prologue, that issued the copy of tile j + 2)
+            for (bool after_copy = true; j <= n_kt - 2; ++j, after_copy = false)
+                masked(j, after_copy, SAFE);
             // last tile jl: no copy in flight, no product S(jl+1); then its own PV
             {
                 const int jl = n_kt - 1;

@@ -180,8 +180,8 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
         o_strides ? *o_strides : default_strides(packed, hq, lq, head_dim);
     if (!stride_ok(qs) || !stride_ok(ks) || !stride_ok(vs) || !stride_ok(os))
         return MI_ATTN_ERR_LAYOUT;
-    // K/V tiles are fetched with 32-bit offsets from a tile's first row.
-    if (ks.row >= kMaxRowStride || vs.row >= kMaxRowStride)
+    // Q, K and V tiles are fetched with 32-bit offsets from a tile's first row.
+    if (qs.row >= kMaxRowStride || ks.row >= kMaxRowStride || vs.row >= kMaxRowStride)
         return MI_ATTN_ERR_LAYOUT;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
         (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))

@@ -59,7 +59,7 @@ typedef enum mi_attn_status {
                                     Hq % Hkv != 0, size too large            */
     MI_ATTN_ERR_LAYOUT = 3,      /* pointer not 16-byte aligned, stride not a
                                     multiple of 8 elements or negative, or a
-                                    K/V row stride of 2^24 elements or more   */
+                                    Q/K/V row stride of 2^24 elements or more */
     MI_ATTN_ERR_DTYPE = 4,       /* in dtype not F16/BF16, or out dtype not
                                     the in dtype or F32                       */
     MI_ATTN_ERR_UNSUPPORTED = 5, /* head_dim not 64 or 128                    */
@@ -113,7 +113,7 @@ struct ihipStream_t;   /* hipStream_t; NULL is the default stream */
  * head_dim  64 or 128.
  * *_strides element strides (see mi_attn_strides_t); NULL means contiguous
  *           ([B, H, L, d] dense, [T, H, d] packed).  Strides must be >= 0 and
- *           multiples of 8, K and V row strides below 2^24 elements; base
+ *           multiples of 8, Q, K and V row strides below 2^24 elements; base
  *           pointers must be 16-byte aligned.
  * cu_seqlens_q, cu_seqlens_k  device int32 arrays of B + 1 offsets, both NULL
  *           (dense) or both set (packed).  Their contents are not checked:

@@ -83,6 +83,7 @@ def call(q=A, k=A * 2, v=A * 3, o=A * 4, lse=A * 5, in_dt=0, out_dt=0,
     (dict(ks=Strides(2048, 1020, 64)), 3),
     (dict(vs=Strides(-2048, 1024, 64)), 3),
     (dict(os_=Strides(2048, 1024, -64)), 3),
+    (dict(qs=Strides(0, 64, 1 << 24)), 3),
     (dict(ks=Strides(0, 64, 1 << 24)), 3),
     (dict(vs=Strides(0, 64, 1 << 25)), 3),
 ])
