@@ -66,9 +66,8 @@
 // Causal masking is bottom-right aligned (key j visible to row i iff
 // j <= i + Lk - Lq): key tiles wholly above the diagonal of a q-tile are
 // never loaded, and the per-key mask is applied only on tiles that straddle
-// the diagonal or the key tail.  For causal inputs a work-group may process
-// q-tiles t and n-1-t one after the other, so that every work-group does the
-// same amount of work.
+// the diagonal or the key tail.  Causal q-tiles are ordered so that the work
+// a CU holds at once is about the same everywhere (see the kernel entry).
 //
 // This header holds the kernel template; attn_fwd_mfma_d64.hip and
 // attn_fwd_mfma_d128.hip instantiate it per head dimension, so that each can
@@ -274,8 +273,7 @@ __device__ __forceinline__ lds16_t* ring() {
 
 template <int D, typename Tin, typename Tout, bool CAUSAL>
 __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
-                                             int h, int b, int kt_lo, int kt_hi,
-                                             int chunk, int64_t tile_id) {
+                                             int h, int b) {
     using L = Layout<D>;
     constexpr int BN = L::BN, KQ = L::KQ;
     constexpr int NKC = L::NKC, NKS = L::NKS, NDB = L::NDB;
@@ -327,15 +325,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                          (packed ? 0 : (int64_t)b * p.v_sb) +
                          (int64_t)g * p.v_sh + (int64_t)k0 * p.v_sr;
 
-    // Key tiles this q-tile needs, and the range [kt0, kt1) of them this
-    // work-group takes: all of them (kt_hi < 0), or one of the two chunks
-    // of a split q-tile (chunk 0 or 1, partial result under tile_id).
+    // Key tiles this q-tile needs: keys [0, kend) in tiles of BN.
     int kend = lk_b;
     if (CAUSAL) kend = min(kend, row0 + kBM + diag);
-    const int n_kt_all = kend > 0 ? (kend + BN - 1) / BN : 0;
-    const int kt0 = kt_hi < 0 ? 0 : kt_lo;
-    const int kt1 = kt_hi < 0 ? n_kt_all : min(kt_hi, n_kt_all);
-    const int n_kt = kt1 - kt0;          // steps of this work-group
+    const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
 
     // Q fragments (B operand of S^T = K Q^T) of the wave's two row blocks:
     // lane holds row `col` of block rb, columns ks*16 + 8*hi .. +7.
@@ -432,7 +425,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     // Buffer resource: base address (48 bits, stride 0), range in bytes, and
     // the fourth word of a raw 32-bit buffer.
     auto tile_rsrc = [&](int kt) {
-        const int rows = kt < kt1 ? min(lk_b - kt * BN, BN) : 0;
+        const int rows = kt < n_kt ? min(lk_b - kt * BN, BN) : 0;
         const uint64_t a = reinterpret_cast<uint64_t>(dma_base + (int64_t)kt * BN * dma_sr);
         u32x4_t r;
         r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
@@ -767,7 +760,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         n_full = min(n_full, lim > 0 ? lim / BN : 0);
     }
 
-    // Step j (0 <= j <= n_kt - 2) works on tile kt0 + j, which lives in stage
+    // Step j (0 <= j <= n_kt - 2) works on tile j, which lives in stage
     // j % STAGES.  K of tile j+1 and V of tile j-1 are read here.  The stage refilled here,
     // (j + AHEAD) % STAGES = (j-2) % STAGES, was last read (V of tile j-2)
     // one step ago, and those fragments were consumed by products of that
@@ -775,7 +768,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     // barrier.
     //   steady: stage S = j % STAGES known at compile time, no mask; FIRST
     //           (j == 0) has no P(j-1) V(j-1).
-    //   masked: any kt0 + j >= n_full, stages picked at run time.
+    //   masked: any j >= n_full, stages picked at run time.
     auto steady = [&](int j, auto SI, auto FIRST, auto SAFE) {
         constexpr int S = decltype(SI)::value;
         constexpr bool first = decltype(FIRST)::value;
@@ -790,8 +783,8 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         u32x4_t kf[NKS];
         read_k(ring<D, (S + 1) % STAGES>(), kf);
         f32x16_t s_new[2];
-        compute(kt0 + j, std::true_type(), std::integral_constant<bool, !first>(),
-                std::false_type(), SAFE, kf, s_new, kt0 + j + AHEAD,
+        compute(j, std::true_type(), std::integral_constant<bool, !first>(),
+                std::false_type(), SAFE, kf, s_new, j + AHEAD,
                 ring<D, (S + AHEAD) % STAGES>(), ring<D, S>());
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s_cur[rb] = s_new[rb];
@@ -808,8 +801,8 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         u32x4_t kf[NKS];
         read_k(stage_of(j + 1), kf);
         f32x16_t s_new[2];               // (j = 0: P(j-1) = 0 and V = 0)
-        compute(kt0 + j, std::true_type(), std::true_type(), std::true_type(), SAFE,
-                kf, s_new, kt0 + j + AHEAD, stage_of(j + AHEAD), stage_of(j));
+        compute(j, std::true_type(), std::true_type(), std::true_type(), SAFE,
+                kf, s_new, j + AHEAD, stage_of(j + AHEAD), stage_of(j));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s_cur[rb] = s_new[rb];
     };
@@ -822,13 +815,13 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             // and tile 0 landed; S(0)
             // (tile 2 only after the barrier: less traffic in flight while
             // every work-group waits for its first tile)
-            issue_tile(kt0, ring<D, 0>());
+            issue_tile(0, ring<D, 0>());
             issue_q();
-            issue_tile(kt0 + 1, ring<D, 1>());
+            issue_tile(1, ring<D, 1>());
             static_assert(AHEAD == 3, "prologue copies");
             wait_vm<DPW>();              // tile 0 and Q in; tile 1 may be pending
             __builtin_amdgcn_s_barrier();
-            issue_tile(kt0 + 2, ring<D, 2>());
+            issue_tile(2, ring<D, 2>());
             read_q();
             if (p.negate_q) {                // scale < 0: fold the sign into q
 #pragma unroll
@@ -849,7 +842,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             }
             // references from the first tile's row maxima (its masked scores
             // excluded); every step then takes the short form of the softmax
-            if (kt0 >= n_full) mask_cur(kt0);
+            if (n_full == 0) mask_cur(0);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
                 const f32x16_t& x = s_cur[rb];
@@ -865,7 +858,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             static_assert(STAGES == 5, "unrolling below");
             // unmasked steps 0 .. n_un-1: step 0, then rounds of STAGES steps
             // starting at stage 1, then the remainder
-            const int n_un = max(0, min(n_full - kt0, n_kt - 1));
+            const int n_un = max(0, min(n_full, n_kt - 1));
             int j = 0;
             if (n_un >= 1) steady(j++, I0(), std::true_type(), SAFE);
             for (; j + STAGES <= n_un; j += STAGES) {
@@ -901,11 +894,11 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 f32x16_t s_unused[2];
                 // vf holds V(jl-1) (zeros if jl = 0); compute reads V(jl)
                 const lds16_t* cur = stage_of(jl);
-                if (kt0 + jl >= n_full)
-                    compute(kt0 + jl, std::false_type(), std::true_type(), std::true_type(),
+                if (jl >= n_full)
+                    compute(jl, std::false_type(), std::true_type(), std::true_type(),
                             SAFE, kf_unused, s_unused, 0, ring<D, 0>(), cur);
                 else
-                    compute(kt0 + jl, std::false_type(), std::true_type(), std::false_type(),
+                    compute(jl, std::false_type(), std::true_type(), std::false_type(),
                             SAFE, kf_unused, s_unused, 0, ring<D, 0>(), cur);
                 pv_last();
             }
@@ -1057,149 +1050,33 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     Block blk[BPW];
 #pragma unroll
     for (int i = 0; i < BPW; ++i) blk[i] = combine(kq * BPW + i);
-    if (chunk < 0) {
 #pragma unroll
-        for (int i = 0; i < BPW; ++i) store(kq * BPW + i, blk[i]);
-        return;
-    }
-    // Split q-tile (two chunks).  Every chunk stores its partial result (o,
-    // mu, lf, lrf per lane of each output block); the chunk that counts last
-    // merges the other's with its own by the same rule, stores O and LSE and
-    // resets the counter for the next call.
-    constexpr int kMaxChunks = 2;
-    constexpr int kFields = 19;          // o[16], mu, lf, lrf
-    auto part = [&](int c, int bi, int k) {   // chunk, row half, block, field
-        return p.split_ws +
-               ((((tile_id * kMaxChunks + c) * 2 + rh) * (2 * NDB) + bi) * kFields + k) *
-                   64 +
-               lane;
-    };
-    // Device-coherent accesses, no cache-wide fences: the partials are
-    // written and read as device-scope relaxed atomics, the stores have
-    // completed (vmcnt 0) before any wave passes the barrier ahead of the
-    // count, and the count is a device-scope atomic.
-    auto put = [&](float* a, float x) {
-        __hip_atomic_store(a, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    auto get = [&](float* a) {
-        return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-        const int bi = kq * BPW + i;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) put(part(chunk, bi, k), blk[i].o[k]);
-        put(part(chunk, bi, 16), blk[i].mu);
-        put(part(chunk, bi, 17), blk[i].lf);
-        put(part(chunk, bi, 18), blk[i].lrf);
-    }
-    wait_vm<0>();                        // this wave's partial is in memory
-    __syncthreads();
-    lds_f32_t* flag = reinterpret_cast<lds_f32_t*>(ring<D, STAGES - 1>()) +
-                      (L::STAGE / 2 - 1);   // last word of the stage
-    if (wave == 0 && lane == 0) {
-        const int before = __hip_atomic_fetch_add(p.split_cnt + tile_id, 1,
-                                                  __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-        *flag = before == kMaxChunks - 1 ? 1.0f : 0.0f;
-    }
-    __syncthreads();
-    if (*flag == 0.0f) return;           // the other chunk finishes the q-tile
-    // chunk 0's partial first and chunk 1's second, whichever work-group
-    // merges, so that repeated calls give identical bits
-    const int other = 1 - chunk;
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-        const int bi = kq * BPW + i;
-        Block x;
-        x.mu = get(part(other, bi, 16));
-        x.lf = get(part(other, bi, 17));
-        x.lrf = get(part(other, bi, 18));
-#pragma unroll
-        for (int k = 0; k < 16; ++k) x.o[k] = get(part(other, bi, k));
-        const Block& a = chunk == 0 ? blk[i] : x;
-        const Block& c = chunk == 0 ? x : blk[i];
-        Block r;
-        r.mu = max2(a.mu, c.mu);
-        const float fa = fast_exp2(a.mu - r.mu), fc = fast_exp2(c.mu - r.mu);
-        r.lf = a.lf * fa + c.lf * fc;
-        r.lrf = a.lrf * fa + c.lrf * fc;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) r.o[k] = a.o[k] * fa + c.o[k] * fc;
-        store(bi, r);
-    }
-    if (wave == 0 && lane == 0)          // ready for the next call
-        __hip_atomic_store(p.split_cnt + tile_id, 0, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < BPW; ++i) store(kq * BPW + i, blk[i]);
 }
 
-// Key tiles of q-tile t of a dense causal input.
-template <int D>
-__device__ __host__ inline int causal_key_tiles(const FwdParams& p, int t) {
-    const int64_t kend = std::min<int64_t>(p.lk, (int64_t)(t + 1) * kBM + p.lk - p.lq);
-    return kend > 0 ? (int)((kend + Layout<D>::BN - 1) / Layout<D>::BN) : 0;
-}
-
-// Split point of causal pair i (q-tiles h = n-1-i and l = i, n q-tiles): the
-// first x key tiles of h form one item, q-tile l and the rest of h the
-// other, so both take about (tiles(h) + tiles(l) + extra) / 2 steps, extra
-// being the cost of the second item's second q-tile in steps.  x = tiles(h)
-// (no split) when l alone is already that long.
-template <int D>
-__device__ __host__ inline int causal_pair_split(const FwdParams& p, int n, int i) {
-    const int th = causal_key_tiles<D>(p, n - 1 - i);
-    const int tl = causal_key_tiles<D>(p, i);
-    const int x = (th + tl + p.pair_extra + 1) / 2;
-    return x < (th + 1) / 2 ? (th + 1) / 2 : x > th ? th : x;
-}
-
-// Grid: blockIdx.x = item * (hq * batch) + (batch, head) index, so that
-// consecutive work-groups take the same item of different heads.
+// Grid (x, y, z) = (query head, batch, item), dispatched x fastest, so that
+// consecutive work-groups take the same item of different heads (the
+// q-tiles of one head then share one XCD when the head count is a multiple
+// of the XCD count).
 //   non-causal: item = q-tile.
-//   causal, pair_split (dense inputs): items 2i and 2i+1 share the work of
-//     q-tiles n-1-i and i (see causal_pair_split); item 2i takes the first
-//     x key tiles of q-tile n-1-i, item 2i+1 q-tile i and then the rest of
-//     q-tile n-1-i; the two partial results of a split q-tile are merged
-//     through the workspace.  The middle q-tile of an odd count is item
-//     n-1, alone.
-//   causal otherwise: q-tiles heaviest first; with `pair` 1 item t covers
-//     q-tiles n-1-t and t; with `pair` 2 the first half of the grid goes
-//     heaviest-first and the second half lightest-first.
+//   causal: q-tiles heaviest first; with `pair` 1 item t covers q-tiles
+//     n-1-t and t one after the other; with `pair` 2 the first half of the
+//     items goes heaviest-first and the second half lightest-first, so that
+//     the two work-groups a CU holds (dispatched half a grid apart) sum to
+//     about the same work everywhere.
 template <int D, typename Tin, typename Tout, bool CAUSAL>
 __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn_fwd_mfma_kernel(
     FwdParams p, int n_qtiles, int pair) {
     // every argument the work-group reads, requested in one round trip
-    // (otherwise the item decode's wait splits them into two)
     asm volatile("" ::"s"(p.q), "s"(p.k), "s"(p.v), "s"(p.o), "s"(p.lse),
                  "s"(p.q_sh), "s"(p.k_sh), "s"(p.v_sh), "s"(p.q_sr), "s"(p.k_sr),
                  "s"(p.v_sr), "s"(p.o_sh), "s"(p.o_sr), "s"(p.lq), "s"(p.lk),
                  "s"(p.group), "s"(p.scale_log2));
-    const int bh_count = p.hq * p.batch;
-    const int item = (int)blockIdx.x / bh_count;
-    const int bh = (int)blockIdx.x - item * bh_count;
-    const int h = bh % p.hq;
-    const int b = bh / p.hq;
-    // up to two parts: q-tile, key range (hi < 0: all), chunk (-1: whole)
-    int tile[2] = {item, -1}, lo[2] = {0, 0}, hi[2] = {-1, -1}, chunk[2] = {-1, -1};
-    int64_t tile_id = 0;
-    if (CAUSAL && p.pair_split) {
-        const int n = n_qtiles;
-        if ((n & 1) && item == n - 1) {
-            tile[0] = n / 2;
-        } else {
-            const int i = item >> 1;
-            const int th = causal_key_tiles<D>(p, n - 1 - i);
-            const int x = causal_pair_split<D>(p, n, i);
-            tile_id = (int64_t)bh * (n / 2) + i;
-            if ((item & 1) == 0) {
-                tile[0] = n - 1 - i;
-                if (x < th) { lo[0] = 0; hi[0] = x; chunk[0] = 0; }
-            } else {
-                tile[0] = i;
-                if (x < th) { tile[1] = n - 1 - i; lo[1] = x; hi[1] = th; chunk[1] = 1; }
-            }
-        }
-    } else if (CAUSAL) {
+    const int h = (int)blockIdx.x;
+    const int b = (int)blockIdx.y;
+    const int item = (int)blockIdx.z;
+    int tile[2] = {item, -1};            // q-tiles of this work-group, in order
+    if (CAUSAL) {
         if (pair == 2) {
             const int half = n_qtiles / 2;
             tile[0] = item < half ? n_qtiles - 1 - item : item - half;
@@ -1210,53 +1087,28 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
     }
     for (int it = 0; it < 2 && tile[it] >= 0; ++it) {
         if (it > 0) __syncthreads();     // the LDS stages are reused
-        attend_qtile<D, Tin, Tout, CAUSAL>(p, tile[it], h, b, lo[it], hi[it],
-                                           chunk[it], tile_id);
+        attend_qtile<D, Tin, Tout, CAUSAL>(p, tile[it], h, b);
     }
 }
 
 template <int D, typename Tin, typename Tout>
 hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
     const int n_qtiles = (p.lq + kBM - 1) / kBM;
-    // causal q-tile order without the pair split: with two resident
-    // work-groups per CU, grid halves heaviest-first and lightest-first;
-    // with one, q-tile pairs
+    // causal q-tile order: with two resident work-groups per CU, grid
+    // halves heaviest-first and lightest-first; with one, q-tile pairs
     const int pair = !p.causal ? 0
                      : p.causal_pairs >= 0 ? p.causal_pairs
                      : (Layout<D>::WG_PER_CU == 2 ? 2 : 1);
-    const int items = (p.causal && !p.pair_split && pair == 1) ? (n_qtiles + 1) / 2
-                                                                : n_qtiles;
-    const int64_t blocks = (int64_t)items * p.hq * p.batch;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int items = (p.causal && pair == 1) ? (n_qtiles + 1) / 2 : n_qtiles;
+    // grid limits (y and z below 2^16) are checked by the caller
+    const dim3 grid((unsigned)p.hq, (unsigned)p.batch, (unsigned)items);
     if (p.causal)
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true>),
-                           dim3((unsigned)blocks), dim3(Layout<D>::THREADS), 0,
-                           stream, p, n_qtiles, pair);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true>), grid,
+                           dim3(Layout<D>::THREADS), 0, stream, p, n_qtiles, pair);
     else
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, false>),
-                           dim3((unsigned)blocks), dim3(Layout<D>::THREADS), 0,
-                           stream, p, n_qtiles, 0);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, false>), grid,
+                           dim3(Layout<D>::THREADS), 0, stream, p, n_qtiles, 0);
     return hipGetLastError();
-}
-
-// Pairs of a causal launch with the pair split whose first q-tile is split
-// (they need a workspace slot), per (batch, head); 0 = the split changes
-// nothing.
-template <int D>
-int causal_split_pairs(const FwdParams& p) {
-    if (!p.causal || p.cu_q != nullptr || p.lq <= 0 || p.lk <= 0) return 0;
-    const int n = (p.lq + kBM - 1) / kBM;
-    int any = 0;
-    for (int i = 0; i < n / 2; ++i)
-        if (causal_pair_split<D>(p, n, i) < causal_key_tiles<D>(p, n - 1 - i)) any = 1;
-    return any ? n / 2 : 0;
-}
-
-// Workspace floats per split q-tile, in the order of the kernel's partial
-// results (2 chunks x 2 row halves x output blocks x 19 fields x 64 lanes).
-template <int D>
-constexpr int64_t split_floats_per_tile() {
-    return 2 * 2 * (2 * Layout<D>::NDB) * 19 * 64;
 }
 
 template <int D>

@@ -8,8 +8,4 @@ hipError_t launch_mfma_d128(const FwdParams& p, int in_dtype, int out_dtype,
     return launch_d<128>(p, in_dtype, out_dtype, stream);
 }
 
-int causal_split_pairs_d128(const FwdParams& p) { return causal_split_pairs<128>(p); }
-
-int64_t split_floats_per_tile_d128() { return split_floats_per_tile<128>(); }
-
 }  // namespace mi_attn

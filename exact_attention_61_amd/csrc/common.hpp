@@ -27,16 +27,6 @@ struct FwdParams {
     int32_t negate_q;                // 1 when scale < 0 (fold the sign into q)
     int32_t causal;
     int32_t causal_pairs;            // causal q-tile order (0, 1, 2; -1 default)
-    // Pair split of dense causal inputs: q-tiles n-1-i and i are shared by
-    // two work-groups of about equal length; a q-tile split between them
-    // leaves two partial results in split_ws (indexed by (batch, head,
-    // pair)) and the later work-group merges them and resets the pair's
-    // counter in split_cnt.  pair_extra: the second q-tile's fixed cost in
-    // key tiles.  0 = off (split_ws, split_cnt unused).
-    int32_t pair_split;
-    int32_t pair_extra;
-    float* split_ws;
-    int32_t* split_cnt;
 };
 
 // Storage tags for the element types (16-bit values are kept as raw bits).
@@ -89,12 +79,5 @@ hipError_t launch_mfma_d64(const FwdParams& p, int in_dtype, int out_dtype,
                           hipStream_t stream);
 hipError_t launch_mfma_d128(const FwdParams& p, int in_dtype, int out_dtype,
                            hipStream_t stream);
-// Pair split of the MFMA kernel: pairs per (batch, head) that need a
-// workspace slot (0: the split changes nothing) and the workspace floats
-// per slot.
-int causal_split_pairs_d64(const FwdParams& p);
-int causal_split_pairs_d128(const FwdParams& p);
-int64_t split_floats_per_tile_d64();
-int64_t split_floats_per_tile_d128();
 
 }  // namespace mi_attn

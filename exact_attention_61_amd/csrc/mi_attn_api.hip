@@ -9,9 +9,6 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
-#include <map>
-#include <mutex>
-#include <utility>
 
 #include "../../include/mi_attn.h"
 #include "common.hpp"
@@ -21,6 +18,7 @@ namespace {
 thread_local int32_t g_last_hip_error = 0;
 
 constexpr int64_t kMaxRowStride = int64_t(1) << 24;   // elements
+constexpr int32_t kMaxQueryRows = 65535 * 128;        // 65535 q-tiles of 128 rows
 
 bool aligned16(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
@@ -45,88 +43,12 @@ bool use_scalar_kernel() {
 // q-tile per work-group, heaviest first; 1 = q-tiles t and n-1-t in one
 // work-group; 2 = one q-tile per work-group, first half of the grid heaviest
 // first and second half lightest first; unset (-1) = the kernel's default
-// for the head dimension.
+// for the head dimension.  Read on every call.
 int causal_pairs_setting() {
-    static const int v = [] {
-        const char* e = std::getenv("MI_ATTN_CAUSAL_PAIRS");
-        if (e == nullptr) return -1;
-        const int x = std::atoi(e);
-        return (x >= 0 && x <= 2) ? x : -1;
-    }();
-    return v;
-}
-
-// Pair split of dense causal inputs (see FwdParams): MI_ATTN_SPLIT=1 turns
-// it on (read on every call).  Off by default: at the sizes measured so far
-// the second q-tile's fixed cost and the hand-over of the partial results
-// outweigh the better balance.  MI_ATTN_PAIR_EXTRA overrides the second
-// q-tile's fixed cost in key tiles (default 4).
-bool split_enabled() {
-    const char* e = std::getenv("MI_ATTN_SPLIT");
-    return e != nullptr && std::strcmp(e, "1") == 0;
-}
-
-int pair_extra_setting() {
-    const char* e = std::getenv("MI_ATTN_PAIR_EXTRA");
-    if (e == nullptr) return 4;
+    const char* e = std::getenv("MI_ATTN_CAUSAL_PAIRS");
+    if (e == nullptr) return -1;
     const int x = std::atoi(e);
-    return x >= 0 && x <= 64 ? x : 4;
-}
-
-// Workspace of the causal pair split, one per device, in kSplitRegions
-// regions used in turn, one per call: calls in flight at once (several
-// streams, or one graph's launches) use different regions as long as at most
-// kSplitRegions of them overlap.  A region's counters are back at zero when
-// its launch ends.  The workspace grows outside stream capture only
-// (allocation and the one-time zeroing of the counters are not capturable);
-// a capturing call that needs more than it has runs without the split.  It
-// is held until the process ends.
-constexpr int kSplitRegions = 4;
-
-struct SplitWs {
-    float* ws = nullptr;
-    int32_t* cnt = nullptr;
-    int64_t region_floats = 0, region_ints = 0;
-    unsigned next = 0;
-};
-
-bool split_workspace(hipStream_t stream, int64_t ws_floats, int64_t cnt_ints,
-                     float** ws, int32_t** cnt) {
-    static std::mutex mu;
-    static std::map<int, SplitWs> table;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return false;
-    std::lock_guard<std::mutex> lock(mu);
-    SplitWs& w = table[dev];
-    if (w.region_floats < ws_floats || w.region_ints < cnt_ints) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(stream, &cs) != hipSuccess ||
-            cs != hipStreamCaptureStatusNone)
-            return false;
-        // every earlier launch on this device may still use the old regions
-        if (hipDeviceSynchronize() != hipSuccess) return false;
-        if (w.ws) (void)hipFree(w.ws);
-        if (w.cnt) (void)hipFree(w.cnt);
-        w = SplitWs{};
-        float* nws = nullptr;
-        int32_t* ncnt = nullptr;
-        if (hipMalloc(&nws, kSplitRegions * ws_floats * sizeof(float)) != hipSuccess)
-            return false;
-        if (hipMalloc(&ncnt, kSplitRegions * cnt_ints * sizeof(int32_t)) != hipSuccess ||
-            hipMemset(ncnt, 0, kSplitRegions * cnt_ints * sizeof(int32_t)) != hipSuccess) {
-            (void)hipFree(nws);
-            if (ncnt) (void)hipFree(ncnt);
-            return false;
-        }
-        w.ws = nws;
-        w.cnt = ncnt;
-        w.region_floats = ws_floats;
-        w.region_ints = cnt_ints;
-    }
-    const unsigned r = w.next++ % kSplitRegions;
-    *ws = w.ws + r * w.region_floats;
-    *cnt = w.cnt + r * w.region_ints;
-    return true;
+    return (x >= 0 && x <= 2) ? x : -1;
 }
 
 mi_attn_strides_t default_strides(bool packed, int64_t heads, int64_t rows,
@@ -156,8 +78,9 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
         return MI_ATTN_ERR_DTYPE;
     if (batch < 0 || lq < 0 || lk < 0 || hq < 1 || hkv < 1 || hq % hkv != 0)
         return MI_ATTN_ERR_SHAPE;
-    // Launch-size limits: work-groups along each grid axis stay below 2^31.
-    if (hq > 65535 || batch > 65535) return MI_ATTN_ERR_SHAPE;
+    // Launch-size limits: the grid is (query head, batch, 128-row q-tile),
+    // at most 65535 along each axis.
+    if (hq > 65535 || batch > 65535 || lq > kMaxQueryRows) return MI_ATTN_ERR_SHAPE;
     if (head_dim != 64 && head_dim != 128) return MI_ATTN_ERR_UNSUPPORTED;
     if (!std::isfinite(scale)) return MI_ATTN_ERR_ARG;
     if (causal != 0 && causal != 1) return MI_ATTN_ERR_ARG;
@@ -214,19 +137,6 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
     p.causal_pairs = causal_pairs_setting();
 
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    p.pair_split = 0;
-    p.pair_extra = pair_extra_setting();
-    p.split_ws = nullptr;
-    p.split_cnt = nullptr;
-    if (!use_scalar_kernel() && split_enabled() && causal && !packed) {
-        const int np = head_dim == 64 ? mi_attn::causal_split_pairs_d64(p)
-                                      : mi_attn::causal_split_pairs_d128(p);
-        const int64_t per = head_dim == 64 ? mi_attn::split_floats_per_tile_d64()
-                                           : mi_attn::split_floats_per_tile_d128();
-        const int64_t slots = (int64_t)batch * hq * np;
-        if (np > 0 && split_workspace(st, slots * per, slots, &p.split_ws, &p.split_cnt))
-            p.pair_split = 1;
-    }
     const hipError_t err =
         use_scalar_kernel()
             ? mi_attn::launch_simple(p, (int)in_dtype, (int)out_dtype,

@@ -56,7 +56,8 @@ typedef enum mi_attn_status {
     MI_ATTN_OK = 0,
     MI_ATTN_ERR_NULL = 1,        /* q, k, v or o is NULL where rows exist     */
     MI_ATTN_ERR_SHAPE = 2,       /* negative size, Hq or Hkv < 1,
-                                    Hq % Hkv != 0, size too large            */
+                                    Hq % Hkv != 0, Hq or B above 65535, or
+                                    lq above 65535 * 128 = 8388480          */
     MI_ATTN_ERR_LAYOUT = 3,      /* pointer not 16-byte aligned, stride not a
                                     multiple of 8 elements or negative, or a
                                     Q/K/V row stride of 2^24 elements or more */
@@ -109,7 +110,8 @@ struct ihipStream_t;   /* hipStream_t; NULL is the default stream */
  *           NULL.  k and v may also be NULL for a dense call with Lk == 0.
  * hq, hkv   query and key/value heads, hkv >= 1, hq a multiple of hkv.
  * lq, lk    dense: sequence lengths (>= 0); packed: the longest query / key
- *           sequence (max_seqlen), used to size the launch.
+ *           sequence (max_seqlen), used to size the launch.  lq <= 8388480
+ *           (65535 tiles of 128 query rows).
  * head_dim  64 or 128.
  * *_strides element strides (see mi_attn_strides_t); NULL means contiguous
  *           ([B, H, L, d] dense, [T, H, d] packed).  Strides must be >= 0 and

@@ -349,15 +349,14 @@ def test_repeat_runs_are_bit_identical():
 
 
 # ---------------------------------------------------------------------------
-# Pair split of dense causal inputs (MI_ATTN_SPLIT=1): q-tiles n-1-i and i are
-# shared by two work-groups; the heavy q-tile's first key tiles go to one,
-# the light q-tile and the rest of the heavy one to the other, and the later
-# of the two merges the heavy q-tile's partial results.  MI_ATTN_PAIR_EXTRA
-# moves the split point; head counts that are not multiples of 8 put the
-# two halves on different XCDs, so the hand-over is checked across them.
+# Causal shapes around the q-tile pairing: head counts that are not multiples
+# of 8, Lq != Lk both ways (bottom-right alignment, rows with no key), an odd
+# q-tile count, and every causal q-tile order the kernel has
+# (MI_ATTN_CAUSAL_PAIRS: 0 heaviest first, 1 q-tiles t and n-1-t in one
+# work-group, 2 grid halves heaviest-first and lightest-first).
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("extra", ["0", "4", "16"])
+@pytest.mark.parametrize("order", ["0", "1", "2"])
 @pytest.mark.parametrize("b,h,lq,lk,d,dtype", [
     (1, 3, 1024, 1024, 64, F16),
     (2, 5, 1024, 1024, 64, BF16),
@@ -367,32 +366,7 @@ def test_repeat_runs_are_bit_identical():
     (1, 2, 1152, 1152, 64, F16),     # odd q-tile count: the middle one alone
     (1, 2, 2048, 2048, 128, F16),
 ])
-def test_pair_split_causal(monkeypatch, extra, b, h, lq, lk, d, dtype):
-    monkeypatch.setenv("MI_ATTN_SPLIT", "1")
-    monkeypatch.setenv("MI_ATTN_PAIR_EXTRA", extra)
-    note(f"pair split extra {extra} b{b} h{h} lq{lq} lk{lk} d{d} {dtype}")
+def test_causal_tile_orders(monkeypatch, order, b, h, lq, lk, d, dtype):
+    monkeypatch.setenv("MI_ATTN_CAUSAL_PAIRS", order)
+    note(f"causal order {order} b{b} h{h} lq{lq} lk{lk} d{d} {dtype}")
     dense_case(b, h, h, lq, lk, d, dtype, True)
-
-
-@pytest.mark.parametrize("b,h,lq,lk,d,dtype", [
-    (1, 3, 1024, 1024, 64, F16),
-    (1, 3, 700, 1100, 128, BF16),
-])
-def test_causal_without_pair_split(monkeypatch, b, h, lq, lk, d, dtype):
-    monkeypatch.setenv("MI_ATTN_SPLIT", "0")
-    note(f"no pair split b{b} h{h} lq{lq} lk{lk} d{d} {dtype}")
-    dense_case(b, h, h, lq, lk, d, dtype, True)
-
-
-def test_pair_split_repeat_runs_are_bit_identical(monkeypatch):
-    monkeypatch.setenv("MI_ATTN_SPLIT", "1")
-    note("pair split determinism")
-    inp = workloads.make("causal_b2h16", seed=1)
-    o1, l1 = run_gpu(inp["q"], inp["k"], inp["v"], causal=True, scale=0.125)
-    o2, l2 = run_gpu(inp["q"], inp["k"], inp["v"], causal=True, scale=0.125)
-    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
-    o_ref, l_ref = oracle.attention(workloads.to_f64(inp["q"]),
-                                    workloads.to_f64(inp["k"]),
-                                    workloads.to_f64(inp["v"]), scale=0.125,
-                                    causal=True)
-    compare(o1, l1, o_ref, l_ref)
