@@ -878,13 +878,14 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     };
     run_keys(std::false_type());
 
-    // Merge of the KQ waves that share a row half.  Every wave stores its
-    // (m, l, lr) and accumulators, relative to its own reference max, in
-    // LDS; then each of them finishes 2*NDB/KQ of the half's 2*NDB output
-    // blocks (row block rb, 32-column block db):
-    //   m = max_q m_q,  x = sum_q x_q 2^(m_q - m).
+    // Merge of the two waves that share a row half (key groups kq = 0, 1).
+    // Wave kq finishes row block rb = kq of the half (all NDB column
+    // blocks): it publishes in LDS only the other row block's accumulators
+    // and (m, l, lr), relative to its own reference max, for its partner,
+    // and takes its own share from registers:
+    //   m = max(m_0, m_1),  x = x_0 2^(m_0 - m) + x_1 2^(m_1 - m).
     constexpr int SPS = L::SLOTS_PER_STAGE;
-    constexpr int BPW = 2 * NDB / KQ;    // output blocks per wave
+    static_assert(KQ == 2, "two key groups per row half");
     auto slot_acc = [&](int w) {
         lds16_t* base = ring<D, 0>();
         const int si = w / SPS;
@@ -902,14 +903,15 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         return reinterpret_cast<lds_f32_t*>(ring<D, STAGES - 1>()) + (L::STAGE / 2 - 2 - w);
     };
     static_assert(L::WAVES * 2 * 3 * 64 + L::WAVES + 1 <= L::STAGE / 2, "flags");
-    // Every wave stores its accumulators and statistics and whether its
-    // short-form sums overflowed (inf or NaN: they only grow).
+    // Every wave stores the partner's row block (accumulators and
+    // statistics) and whether its short-form sums overflowed (inf or NaN:
+    // they only grow).
     auto publish = [&]() {
         __syncthreads();                 // every wave is done with the ring
         refresh_lane();
         lds_f4_t* a = slot_acc(wave);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        auto put = [&](auto RBc) {
+            constexpr int rb = decltype(RBc)::value;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -920,7 +922,9 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             stat(wave, rb, 0)[lane] = m[rb];
             stat(wave, rb, 1)[lane] = l[rb];
             stat(wave, rb, 2)[lane] = lr[rb];
-        }
+        };
+        if (kq == 0) put(I1());
+        else put(I0());
         const bool bad = __builtin_amdgcn_ballot_w64(!(lr[0] + lr[1] < __builtin_inff())) != 0;
         if (lane == 0) *ovf_flag(wave) = bad ? 1.0f : 0.0f;
         __syncthreads();
@@ -954,40 +958,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         publish();
     }
 
-    // Merged result of output block bi of this row half, relative to mu.
+    // Merged result of one output block, relative to mu.
     struct Block {
         float mu, lf, lrf;
         f32x16_t o;
-    };
-    auto combine = [&](const int bi) {
-        const int rb = bi / NDB, db = bi % NDB;
-        float mq[KQ];
-        float mt = -__builtin_inff();
-#pragma unroll
-        for (int q = 0; q < KQ; ++q) {
-            mq[q] = stat(rh + 2 * q, rb, 0)[lane];
-            mt = max2(mt, mq[q]);
-        }
-        Block r;
-        r.mu = mt == -__builtin_inff() ? 0.0f : mt;
-        r.lf = 0.0f;
-        r.lrf = 0.0f;
-        r.o = f32x16_t{};
-#pragma unroll
-        for (int q = 0; q < KQ; ++q) {
-            const int w = rh + 2 * q;
-            const float f = fast_exp2(mq[q] - r.mu);
-            r.lf += stat(w, rb, 1)[lane] * f;
-            r.lrf += stat(w, rb, 2)[lane] * f;
-            const lds_f4_t* a = slot_acc(w) + ((rb * NDB + db) * 4) * 64 + lane;
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                const f32x4_t x = a[gg * 64];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) r.o[4 * gg + i] += x[i] * f;
-            }
-        }
-        return r;
     };
     auto store = [&](const int bi, const Block& r) {
         const int rb = bi / NDB, db = bi % NDB;
@@ -1018,12 +992,42 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             }
         }
     };
-    // output blocks bi = kq*BPW + i of this wave
-    Block blk[BPW];
+    // Row block rb = kq: this wave's share from registers, the partner's
+    // (key group 1 - kq) from LDS, summed key group 0 first.
+    auto finish = [&](auto RBc) {
+        constexpr int rb = decltype(RBc)::value;
+        const int wp = rh + 2 * (1 - rb);    // the partner wave
+        const float mp = stat(wp, rb, 0)[lane];
+        const float mt = max2(m[rb], mp);
+        const float mu = mt == -__builtin_inff() ? 0.0f : mt;
+        const float fs = fast_exp2(m[rb] - mu), fp = fast_exp2(mp - mu);
+        const float lp = stat(wp, rb, 1)[lane], lrp = stat(wp, rb, 2)[lane];
+        // (self, partner) in key-group order
+        const float f0 = rb == 0 ? fs : fp, f1 = rb == 0 ? fp : fs;
+        const float l0 = rb == 0 ? l[rb] : lp, l1 = rb == 0 ? lp : l[rb];
+        const float r0 = rb == 0 ? lr[rb] : lrp, r1 = rb == 0 ? lrp : lr[rb];
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) blk[i] = combine(kq * BPW + i);
+        for (int db = 0; db < NDB; ++db) {
+            Block r;
+            r.mu = mu;
+            r.lf = l0 * f0 + l1 * f1;
+            r.lrf = r0 * f0 + r1 * f1;
+            const lds_f4_t* a = slot_acc(wp) + ((rb * NDB + db) * 4) * 64 + lane;
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) store(kq * BPW + i, blk[i]);
+            for (int gg = 0; gg < 4; ++gg) {
+                const f32x4_t x = a[gg * 64];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float own = acc[rb][db][4 * gg + i];
+                    const float x0 = rb == 0 ? own : x[i], x1 = rb == 0 ? x[i] : own;
+                    r.o[4 * gg + i] = x0 * f0 + x1 * f1;
+                }
+            }
+            store(rb * NDB + db, r);
+        }
+    };
+    if (kq == 0) finish(I0());
+    else finish(I1());
 }
 
 // Grid (x, y, z) = (query head, batch, item), dispatched x fastest, so that
@@ -1059,7 +1063,12 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
     }
     for (int it = 0; it < 2 && tile[it] >= 0; ++it) {
         if (it > 0) __syncthreads();     // the LDS stages are reused
-        attend_qtile<D, Tin, Tout, CAUSAL>(p, tile[it], h, b);
+        // head and batch made opaque here: what the q-tile derives from them
+        // is computed inside the iteration, not hoisted out of the loop and
+        // kept live (spilled) across the whole key loop
+        int hh = h, bb = b;
+        asm volatile("" : "+s"(hh), "+s"(bb));
+        attend_qtile<D, Tin, Tout, CAUSAL>(p, tile[it], hh, bb);
     }
 }
 
