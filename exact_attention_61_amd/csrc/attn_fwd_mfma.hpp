@@ -312,7 +312,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     }
     const int row0 = qtile * kBM;
     if (row0 >= lq_b) return;            // uniform over the work-group
-    const int g = h / p.group;
+    // kv head h / group as a multiply-high by ceil(2^32 / group): exact for
+    // h and group below 2^16 (the caller's limit on hq)
+    const int g = (int)(((uint64_t)(uint32_t)h * p.group_magic) >> 32);
+    static_assert(sizeof(p.group_magic) == 8, "64-bit reciprocal");
     const int diag = lk_b - lq_b;        // key j visible to row i iff j <= i + diag
 
     const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) +
@@ -1040,35 +1043,37 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 //     items goes heaviest-first and the second half lightest-first, so that
 //     the two work-groups a CU holds (dispatched half a grid apart) sum to
 //     about the same work everywhere.
-template <int D, typename Tin, typename Tout, bool CAUSAL>
+template <int D, typename Tin, typename Tout, bool CAUSAL, bool PAIRS>
 __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn_fwd_mfma_kernel(
     FwdParams p, int n_qtiles, int pair) {
     // every argument the work-group reads, requested in one round trip
     asm volatile("" ::"s"(p.q), "s"(p.k), "s"(p.v), "s"(p.o), "s"(p.lse),
                  "s"(p.q_sh), "s"(p.k_sh), "s"(p.v_sh), "s"(p.q_sr), "s"(p.k_sr),
                  "s"(p.v_sr), "s"(p.o_sh), "s"(p.o_sr), "s"(p.lq), "s"(p.lk),
-                 "s"(p.group), "s"(p.scale_log2));
+                 "s"(p.group_magic), "s"(p.scale_log2));
     const int h = (int)blockIdx.x;
     const int b = (int)blockIdx.y;
     const int item = (int)blockIdx.z;
-    int tile[2] = {item, -1};            // q-tiles of this work-group, in order
-    if (CAUSAL) {
-        if (pair == 2) {
-            const int half = n_qtiles / 2;
-            tile[0] = item < half ? n_qtiles - 1 - item : item - half;
-        } else {
-            tile[0] = n_qtiles - 1 - item;
-            if (pair == 1 && item < tile[0]) tile[1] = item;
+    if constexpr (!PAIRS) {
+        // one q-tile per work-group: a straight-line body
+        int t = item;
+        if (CAUSAL)
+            t = pair == 2 ? (item < n_qtiles / 2 ? n_qtiles - 1 - item : item - n_qtiles / 2)
+                          : n_qtiles - 1 - item;
+        attend_qtile<D, Tin, Tout, CAUSAL>(p, t, h, b);
+    } else {
+        // causal, q-tiles n-1-item and item one after the other
+        int tile[2] = {n_qtiles - 1 - item, -1};
+        if (item < tile[0]) tile[1] = item;
+        for (int it = 0; it < 2 && tile[it] >= 0; ++it) {
+            if (it > 0) __syncthreads();     // the LDS stages are reused
+            // head and batch made opaque here: what the q-tile derives from
+            // them is computed inside the iteration, not hoisted out of the
+            // loop and kept live (spilled) across the whole key loop
+            int hh = __builtin_amdgcn_readfirstlane(h), bb = __builtin_amdgcn_readfirstlane(b);
+            asm volatile("" : "+s"(hh), "+s"(bb));
+            attend_qtile<D, Tin, Tout, CAUSAL>(p, tile[it], hh, bb);
         }
-    }
-    for (int it = 0; it < 2 && tile[it] >= 0; ++it) {
-        if (it > 0) __syncthreads();     // the LDS stages are reused
-        // head and batch made opaque here: what the q-tile derives from them
-        // is computed inside the iteration, not hoisted out of the loop and
-        // kept live (spilled) across the whole key loop
-        int hh = h, bb = b;
-        asm volatile("" : "+s"(hh), "+s"(bb));
-        attend_qtile<D, Tin, Tout, CAUSAL>(p, tile[it], hh, bb);
     }
 }
 
@@ -1083,11 +1088,14 @@ hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
     const int items = (p.causal && pair == 1) ? (n_qtiles + 1) / 2 : n_qtiles;
     // grid limits (y and z below 2^16) are checked by the caller
     const dim3 grid((unsigned)p.hq, (unsigned)p.batch, (unsigned)items);
-    if (p.causal)
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true>), grid,
+    if (p.causal && pair == 1)
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true, true>), grid,
+                           dim3(Layout<D>::THREADS), 0, stream, p, n_qtiles, pair);
+    else if (p.causal)
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true, false>), grid,
                            dim3(Layout<D>::THREADS), 0, stream, p, n_qtiles, pair);
     else
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, false>), grid,
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, false, false>), grid,
                            dim3(Layout<D>::THREADS), 0, stream, p, n_qtiles, 0);
     return hipGetLastError();
 }

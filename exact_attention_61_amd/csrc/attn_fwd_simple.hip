@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kRows) void attn_fwd_simple_kernel(FwdParams p) {
     if (row0 >= lq_b) return;                       // uniform over the block
     const int r = row0 + (int)threadIdx.x;
     const bool row_ok = r < lq_b;
-    const int g = h / p.group;
+    const int g = h / (p.hq / p.hkv);
     const bool packed = p.cu_q != nullptr;
 
     const Tin* qp = reinterpret_cast<const Tin*>(p.q) +

@@ -21,7 +21,9 @@ struct FwdParams {
     int64_t k_sb, k_sh, k_sr;
     int64_t v_sb, v_sh, v_sr;
     int64_t o_sb, o_sh, o_sr;
-    int32_t batch, hq, hkv, group;   // group = hq / hkv
+    uint64_t group_magic;            // ceil(2^32 / (hq / hkv)): kv head of query
+                                     // head h = (h * group_magic) >> 32
+    int32_t batch, hq, hkv;
     int32_t lq, lk;                  // dense lengths, or the packed maxima
     float scale_log2;                // |scale| * log2(e), in fp32
     int32_t negate_q;                // 1 when scale < 0 (fold the sign into q)

@@ -125,7 +125,12 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
     p.batch = batch;
     p.hq = hq;
     p.hkv = hkv;
-    p.group = hq / hkv;
+    // kv head = h / group, taken in the kernel as (h * ceil(2^32 / group))
+    // >> 32, exact for h and group below 2^16 (hq <= 65535 above)
+    {
+        const uint64_t grp = (uint64_t)(hq / hkv);
+        p.group_magic = ((uint64_t(1) << 32) + grp - 1) / grp;
+    }
     p.lq = lq;
     p.lk = lk;
     // |scale| * log2(e), floored at 1e-30 so that a masked score (-inf) times
