@@ -455,6 +455,15 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         for (int t = 0; t < DPW; ++t) issue_part(rsrc, stage, t);
     };
 
+    // The prologue's copies (tile 0, Q, tile 1) go out before the rest of
+    // the set-up, whose instructions then overlap their latency.
+    auto issue_first = [&]() {
+        issue_tile(0, ring<D, 0>());
+        issue_q();
+        issue_tile(1, ring<D, 1>());
+    };
+    if (n_kt > 0) issue_first();
+
     const float c2 = p.scale_log2;       // |scale| * log2(e)
     float m[2], l[2], lr[2];             // per row block: reference max (log2
     f32x16_t acc[2][NDB];                // domain), this lane's exp-sums, O^T
@@ -792,15 +801,13 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 
     // The key loop: prologue, steps, last tile.  The short form first; the
     // safe form only when the short form overflowed (see compute).
-    auto run_keys = [&](auto SAFE) {
+    auto run_keys = [&](auto SAFE, bool copies_issued) {
         if (n_kt > 0) {
             // prologue: copies of tile 0, Q and tile 1 in flight, then Q
             // and tile 0 landed; S(0)
             // (tile 2 only after the barrier: less traffic in flight while
             // every work-group waits for its first tile)
-            issue_tile(0, ring<D, 0>());
-            issue_q();
-            issue_tile(1, ring<D, 1>());
+            if (!copies_issued) issue_first();
             static_assert(AHEAD == 3, "prologue copies");
             wait_vm<DPW>();              // tile 0 and Q in; tile 1 may be pending
             __builtin_amdgcn_s_barrier();
@@ -879,7 +886,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             }
         }
     };
-    run_keys(std::false_type());
+    run_keys(std::false_type(), true);
 
     // Merge of the two waves that share a row half (key groups kq = 0, 1).
     // Wave kq finishes row block rb = kq of the half (all NDB column
@@ -957,7 +964,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 #pragma unroll
             for (int db = 0; db < NDB; ++db) vf[db][c] = u32x4_t{0u, 0u, 0u, 0u};
         }
-        run_keys(std::true_type());
+        run_keys(std::true_type(), false);
         publish();
     }
 
