@@ -14,16 +14,18 @@
 // row block merge their results at the end.
 //
 // The reference max of a row is set from the first tile's scores; later tiles
-// are exponentiated against it without computing their max.  Only when some
-// lane's 16 probabilities of a row sum to more than 2^10 (or overflow) does
-// the wave recompute the tile's scores, move the references of the rows whose
-// tile max exceeds them to that max and rescale.  Any reference value gives
-// the same O = u / l and LSE = m + log2 l; probabilities stay below 2^10, far
-// inside every range, and the rescale is skipped on almost every tile.  The output is
-// normalised by the sum of the probabilities as rounded for the PV product
-// (one v_dot2 per pair), so that the rounding of a dominant probability
-// cancels between numerator and denominator.  The log-sum-exp uses that sum
-// for fp16 inputs (2^-11 relative at most) and an fp32 sum for bf16 inputs.
+// are exponentiated against it without computing their max (any reference
+// gives the same O = u / l and LSE = m + log2 l, and every row's largest
+// probability is at least 1, so none underflows to a zero sum).  Only an
+// overflow is wrong: a probability past the 16-bit range leaves a lane's fp32
+// row sum at or above that range's maximum, and the work-group then redoes
+// the q-tile in a safe form that moves a row's reference whenever a tile's
+// max exceeds it by more than 2^8.  The row sums are taken in fp32 from the
+// unrounded probabilities.  For fp16 inputs they also normalise the output
+// (rounding P to fp16 moves the product by at most 2^-11 relative); for bf16
+// inputs the output is normalised by the sum of the probabilities as rounded
+// for the PV product (one v_dot2 per pair), so that the rounding of a
+// dominant probability cancels between numerator and denominator.
 //
 // Work decomposition.  A work-group of 4 waves owns BM = 128 query rows of
 // one (batch, head) at a time and walks the keys in tiles of BN = 64 keys.
@@ -105,10 +107,13 @@ template <> struct Mma<f16_t> {
             __builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
             0, 0, 0);
     }
-    // The row sum is taken over the rounded P (v_dot2_f32_f16 with ones):
-    // fp16 rounding moves it by at most 2^-11 relative, i.e. the log-sum-exp
-    // by at most 4.9e-4, and the output normalisation matches the product.
-    static constexpr bool kFp32Sum = false;
+    // O is normalised by the fp32 row sum: fp16 rounding of P moves the
+    // product by at most 2^-11 relative.  A P past the fp16 range can only
+    // occur in a lane whose fp32 sum reaches kPMax, which sends the q-tile to
+    // the safe form.  (The sum of the rounded P would cost one v_dot2 per
+    // pair, and those do not overlap the matrix products.)
+    static constexpr bool kNormRounded = false;
+    static constexpr float kPMax = 65504.0f;
     __device__ __forceinline__ static float add_pair(uint32_t pr, float c) {
         const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
         return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pr), one, c,
@@ -129,9 +134,12 @@ template <> struct Mma<bf16_t> {
             __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
             c, 0, 0, 0);
     }
-    // bf16 rounding is too coarse for the log-sum-exp: it uses an fp32 sum,
-    // the output normalisation the sum of the rounded P.
-    static constexpr bool kFp32Sum = true;
+    // bf16 rounding is too coarse for the log-sum-exp: it uses the fp32
+    // sum, and O is normalised by the sum of the rounded P (v_dot2), so the
+    // rounding of a dominant probability cancels between numerator and
+    // denominator.  kPMax stays below the largest finite bf16.
+    static constexpr bool kNormRounded = true;
+    static constexpr float kPMax = 3.0e38f;
     // c + the two packed bf16 values (exact products with 1, fp32 sum)
     __device__ __forceinline__ static float add_pair(uint32_t pr, float c) {
         const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -611,7 +619,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         if constexpr (!safe) {
             // Part u (0..7) = scores 4 * (u & 3) .. +3 of row block u >> 2:
             // group g exponentiates part g and rounds and sums part g - 1.
-            // The row sums go straight into l and lr.
+            // The row sums go straight into l (fp32) and, for bf16, lr.
             float pe[2][4];              // probabilities of the last two parts
 #pragma unroll
             for (int gi = 0; gi < kGroups; ++gi) {
@@ -624,10 +632,8 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                         x[i] = fast_exp2(fmaf(s_cur[rb][e0 + i], c2, nm[rb]));
                         pin(x[i]);       // computed in this group, not sunk
                     }
-                    if (Mma<Tin>::kFp32Sum) {
-                        l[rb] += (x[0] + x[1]) + (x[2] + x[3]);
-                        pin(l[rb]);
-                    }
+                    l[rb] += (x[0] + x[1]) + (x[2] + x[3]);
+                    pin(l[rb]);
                 }
                 if (gi >= 1) {
                     const int u = gi - 1, rb = u >> 2, c = (u >> 1) & 1, h = u & 1;
@@ -636,8 +642,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                     const uint32_t d = Mma<Tin>::pack(x[2], x[3]);
                     p_new[rb][c][2 * h] = a;
                     p_new[rb][c][2 * h + 1] = d;
-                    lr[rb] = Mma<Tin>::add_pair(d, Mma<Tin>::add_pair(a, lr[rb]));
-                    pin(lr[rb]);
+                    if (Mma<Tin>::kNormRounded) {
+                        lr[rb] = Mma<Tin>::add_pair(d, Mma<Tin>::add_pair(a, lr[rb]));
+                        pin(lr[rb]);
+                    }
                     pin(p_new[rb][c]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -696,10 +704,8 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                         pin(pe[i]);
                         s_cur[rb][e0 + i] = pe[i];
                     }
-                    if (Mma<Tin>::kFp32Sum) {
-                        psum[rb][(gi - 1) >> 1] = (pe[0] + pe[1]) + (pe[2] + pe[3]);
-                        pin(psum[rb][(gi - 1) >> 1]);
-                    }
+                    psum[rb][(gi - 1) >> 1] = (pe[0] + pe[1]) + (pe[2] + pe[3]);
+                    pin(psum[rb][(gi - 1) >> 1]);
                 } else {
                     // P^T operand of 16-key chunk c of row block rb
                     const int rb = (gi - 9) >> 1, c = (gi - 9) & 1;
@@ -708,8 +714,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                     for (int jj = 0; jj < 4; ++jj) {
                         const int e = 8 * c + 2 * jj;
                         p_new[rb][c][jj] = Mma<Tin>::pack(s_cur[rb][e], s_cur[rb][e + 1]);
-                        if (jj & 1) t1 = Mma<Tin>::add_pair(p_new[rb][c][jj], t1);
-                        else t0 = Mma<Tin>::add_pair(p_new[rb][c][jj], t0);
+                        if (Mma<Tin>::kNormRounded) {
+                            if (jj & 1) t1 = Mma<Tin>::add_pair(p_new[rb][c][jj], t1);
+                            else t0 = Mma<Tin>::add_pair(p_new[rb][c][jj], t0);
+                        }
                     }
                     rsr[rb][c] = t0 + t1;
                     pin(p_new[rb][c]);
@@ -724,9 +732,8 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             if (kGroupV >= kGroups) read_v(v_next);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
-                if (Mma<Tin>::kFp32Sum)
-                    l[rb] += (psum[rb][0] + psum[rb][1]) + (psum[rb][2] + psum[rb][3]);
-                lr[rb] += rsr[rb][0] + rsr[rb][1];
+                l[rb] += (psum[rb][0] + psum[rb][1]) + (psum[rb][2] + psum[rb][3]);
+                if (Mma<Tin>::kNormRounded) lr[rb] += rsr[rb][0] + rsr[rb][1];
             }
             // the accumulators hold P(j-1) V(j-1), relative to the old
             // references, only once this step's products are in
@@ -935,7 +942,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         };
         if (kq == 0) put(I1());
         else put(I0());
-        const bool bad = __builtin_amdgcn_ballot_w64(!(lr[0] + lr[1] < __builtin_inff())) != 0;
+        // a probability past the 16-bit range (or an inf / NaN) leaves some
+        // lane's fp32 sum at or above kPMax
+        const bool bad = __builtin_amdgcn_ballot_w64(
+                             !(l[0] < Mma<Tin>::kPMax && l[1] < Mma<Tin>::kPMax)) != 0;
         if (lane == 0) *ovf_flag(wave) = bad ? 1.0f : 0.0f;
         __syncthreads();
     };
@@ -975,10 +985,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     };
     auto store = [&](const int bi, const Block& r) {
         const int rb = bi / NDB, db = bi % NDB;
-        // O is normalised by the sum of the rounded P, LSE uses the fp32 sum
-        // where there is one.
-        const float ln = r.lrf + partner(r.lrf);
-        const float lt = Mma<Tin>::kFp32Sum ? r.lf + partner(r.lf) : ln;
+        // O is normalised by the sum of the rounded P (bf16) or the fp32 sum
+        // (fp16); LSE uses the fp32 sum.
+        const float lt = r.lf + partner(r.lf);
+        const float ln = Mma<Tin>::kNormRounded ? r.lrf + partner(r.lrf) : lt;
         if (qrow(rb) < lq_b) {
             const float inv = ln > 0.0f ? 1.0f / ln : 0.0f;
             const int64_t orow = (packed ? 0 : (int64_t)b * p.o_sb) +

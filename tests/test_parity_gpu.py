@@ -309,6 +309,7 @@ def test_dominant_key():
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype,boost", [
     (F16, 1.5),      # up to ~2^11 above the first tile's max: in range
+    (F16, 4.0),      # around 2^16: some rows just past fp16, others just under
     (F16, 10.0),     # ~2^30 and more: past fp16, redone in the safe form
     (BF16, 10.0),    # in bf16 range
     (BF16, 100.0),   # ~2^300 and more: past fp32, redone in the safe form
