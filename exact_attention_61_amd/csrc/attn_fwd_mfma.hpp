@@ -568,7 +568,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     // kGap does the wave exchange the maxima with lane ^ 32, move the
     // references of the rows whose tile max exceeds them by more than kGap,
     // and rescale (the accumulators after this step's products).
-    auto compute = [&](int j, auto NEXT, auto PV, bool msk, auto SAFE,
+    auto compute = [&](int j, auto NEXT, auto PV, auto MASK, auto SAFE,
                        const u32x4_t (&kf)[NKS], f32x16_t (&s_next)[2],
                        int dma_kt, lds16_t* dma_stage, const lds16_t* v_next) {
         constexpr bool next = decltype(NEXT)::value;
@@ -603,7 +603,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         auto vread_at = [&](int gi) {
             if (gi == kGroupV) read_v(v_next);
         };
-        if (msk) mask_cur(j);            // wave-uniform branch
+        if constexpr (decltype(MASK)::value) mask_cur(j);
         u32x4_t p_new[2][2];             // this tile's P; p_prev stays for PV
         // The copy of tile dma_kt (NEXT only), one instruction every few
         // groups: a burst of copies from every wave at once fills the memory
@@ -776,16 +776,22 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     }
 
     // Step j (0 <= j <= n_kt - 2) works on tile j, which lives in stage
-    // j % STAGES (S, known at compile time: the loop below is unrolled by
-    // STAGES).  K of tile j+1 and V of tile j-1 are read here.  The stage
+    // j % STAGES.  K of tile j+1 and V of tile j-1 are read here.  The stage
     // refilled here, (j + AHEAD) % STAGES = (j-2) % STAGES, was last read
     // (V of tile j-2) one step ago, and those fragments were consumed by
     // products of that step, so every wave is done with it once it reaches
-    // this step's barrier.  FIRST (j == 0) has no P(j-1) V(j-1).  Tiles at
-    // or past n_full hold keys some row of the work-group must not see: the
-    // step masks them (a wave-uniform branch).  Every step issues the copies
-    // of tile j + AHEAD -- past the key range they read nothing -- so the
-    // wait at the top of a step is the same constant count everywhere.
+    // this step's barrier.  Every step issues the copies of tile j + AHEAD
+    // -- past the key range they read nothing -- so the wait at the top of a
+    // step is the same constant count everywhere.
+    //   steady: stage S = j % STAGES known at compile time (the loop below is
+    //           unrolled by STAGES), no mask; FIRST (j == 0) has no
+    //           P(j-1) V(j-1).
+    //   masked: tiles at or past n_full (at most 3 per q-tile, at the end of
+    //           its range) hold keys some row of the work-group must not
+    //           see; stages picked at run time.  Keeping the mask out of the
+    //           unrolled loop keeps the steady step's code as it is (with
+    //           the mask in every step, the d = 128 step gained ~30 % more
+    //           instructions, mostly copies between register files).
     auto steady = [&](int j, auto SI, auto FIRST, auto SAFE) {
         constexpr int S = decltype(SI)::value;
         constexpr bool first = decltype(FIRST)::value;
@@ -800,8 +806,22 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         u32x4_t kf[NKS];
         read_k(ring<D, (S + 1) % STAGES>(), kf);
         f32x16_t s_new[2];
-        compute(j, std::true_type(), std::integral_constant<bool, !first>(), j >= n_full,
+        compute(j, std::true_type(), std::integral_constant<bool, !first>(), std::false_type(),
                 SAFE, kf, s_new, j + AHEAD, ring<D, (S + AHEAD) % STAGES>(), ring<D, S>());
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) s_cur[rb] = s_new[rb];
+    };
+    auto masked = [&](int j, auto SAFE) {
+        wait_vm<(AHEAD - 2) * DPW>();
+        __builtin_amdgcn_s_barrier();
+        refresh_lane();
+        asm volatile("" : "+v"(k_off));
+        asm volatile("" : "+v"(v_off));
+        u32x4_t kf[NKS];
+        read_k(stage_of(j + 1), kf);
+        f32x16_t s_new[2];               // (j = 0: P(j-1) = 0 and V = 0)
+        compute(j, std::true_type(), std::true_type(), std::true_type(), SAFE, kf, s_new,
+                j + AHEAD, stage_of(j + AHEAD), stage_of(j));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s_cur[rb] = s_new[rb];
     };
@@ -853,29 +873,31 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 nm[rb] = m[rb] == -__builtin_inff() ? 0.0f : -m[rb];
             }
             static_assert(STAGES == 5, "unrolling below");
-            // steps 0 .. n_st-1: step 0, then rounds of STAGES steps starting
-            // at stage 1, then the remainder
-            const int n_st = n_kt - 1;
+            // unmasked steps 0 .. n_un-1: step 0, then rounds of STAGES steps
+            // starting at stage 1, then the remainder
+            const int n_un = max(0, min(n_full, n_kt - 1));
             int j = 0;
-            if (n_st >= 1) steady(j++, I0(), std::true_type(), SAFE);
-            for (; j + STAGES <= n_st; j += STAGES) {
+            if (n_un >= 1) steady(j++, I0(), std::true_type(), SAFE);
+            for (; j + STAGES <= n_un; j += STAGES) {
                 steady(j, I1(), std::false_type(), SAFE);
                 steady(j + 1, I2(), std::false_type(), SAFE);
                 steady(j + 2, I3(), std::false_type(), SAFE);
                 steady(j + 3, I4(), std::false_type(), SAFE);
                 steady(j + 4, I0(), std::false_type(), SAFE);
             }
-            // remaining steps (j < n_st), j % STAGES == 1 here
-            if (j < n_st) {
+            // remaining unmasked steps (j < n_un), j % STAGES == 1 here
+            if (j < n_un) {
                 steady(j++, I1(), std::false_type(), SAFE);
-                if (j < n_st) {
+                if (j < n_un) {
                     steady(j++, I2(), std::false_type(), SAFE);
-                    if (j < n_st) {
+                    if (j < n_un) {
                         steady(j++, I3(), std::false_type(), SAFE);
-                        if (j < n_st) steady(j++, I4(), std::false_type(), SAFE);
+                        if (j < n_un) steady(j++, I4(), std::false_type(), SAFE);
                     }
                 }
             }
+            // masked steps up to n_kt - 2
+            for (; j <= n_kt - 2; ++j) masked(j, SAFE);
             // last tile jl: no copy in flight, no product S(jl+1); then its own PV
             {
                 const int jl = n_kt - 1;
@@ -887,8 +909,12 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 f32x16_t s_unused[2];
                 // vf holds V(jl-1) (zeros if jl = 0); compute reads V(jl)
                 const lds16_t* cur = stage_of(jl);
-                compute(jl, std::false_type(), std::true_type(), jl >= n_full, SAFE,
-                        kf_unused, s_unused, 0, ring<D, 0>(), cur);
+                if (jl >= n_full)
+                    compute(jl, std::false_type(), std::true_type(), std::true_type(), SAFE,
+                            kf_unused, s_unused, 0, ring<D, 0>(), cur);
+                else
+                    compute(jl, std::false_type(), std::true_type(), std::false_type(), SAFE,
+                            kf_unused, s_unused, 0, ring<D, 0>(), cur);
                 pv_last();
             }
         }
