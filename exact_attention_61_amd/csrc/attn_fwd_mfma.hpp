@@ -612,7 +612,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             if (next) {
 #pragma unroll
                 for (int t = 0; t < DPW; ++t)
-                    if (gi == 1 + t * (kGroups - 2) / DPW) issue_part(rsrc, dma_stage, t);
+                    if (gi == 2 + t * (kGroups - 3) / DPW) issue_part(rsrc, dma_stage, t);
             }
         };
         const auto rsrc = tile_rsrc(dma_kt);
@@ -1080,7 +1080,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 // consecutive work-groups take the same item of different heads (the
 // q-tiles of one head then share one XCD when the head count is a multiple
 // of the XCD count).
-//   non-causal: item = q-tile.
+//   non-causal: item = q-tile (packed batches: q-tile n-1-item).
 //   causal: q-tiles heaviest first; with `pair` 1 item t covers q-tiles
 //     n-1-t and t one after the other; with `pair` 2 the first half of the
 //     items goes heaviest-first and the second half lightest-first, so that
@@ -1100,6 +1100,9 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
     if constexpr (!PAIRS) {
         // one q-tile per work-group: a straight-line body
         int t = item;
+        // packed batches: highest q-tile index first -- those q-tiles exist
+        // only for the longest sequences, whose work-groups are the heaviest
+        if (p.cu_q != nullptr) t = n_qtiles - 1 - item;
         if (CAUSAL)
             t = pair == 2 ? (item < n_qtiles / 2 ? n_qtiles - 1 - item : item - n_qtiles / 2)
                           : n_qtiles - 1 - item;
