@@ -73,6 +73,7 @@ def call(q=A, k=A * 2, v=A * 3, o=A * 4, lse=A * 5, in_dt=0, out_dt=0,
     (dict(in_dt=0, out_dt=1), 4), (dict(in_dt=1, out_dt=0), 4),
     (dict(b=-1), 2), (dict(lq=-1), 2), (dict(lk=-5), 2), (dict(hq=0), 2),
     (dict(hkv=0), 2), (dict(hq=6, hkv=4), 2), (dict(hq=70000, hkv=1), 2),
+    (dict(b=70000), 2), (dict(lq=65535 * 128 + 1), 2),   # grid axes y and z
     (dict(d=32), 5), (dict(d=96), 5), (dict(d=256), 5), (dict(d=0), 5),
     (dict(scale=math.nan), 6), (dict(scale=math.inf), 6),
     (dict(scale=-math.inf), 6), (dict(causal=2), 6), (dict(causal=-1), 6),
