@@ -39,10 +39,12 @@
 // registers): one work-group per CU.
 //
 // K and V tiles go from global memory straight into LDS (buffer_load_dwordx4
-// ... lds) through a ring of 5 stages, 3 tiles ahead of use, with one
-// barrier per tile.  The stages are separate LDS arrays and the loop is
-// unrolled by 5, so the compiler can see that a fragment read never touches a
-// stage a copy is still landing in.
+// ... lds, written as inline asm) through a ring of 5 stages, 3 tiles ahead
+// of use, with one barrier per tile.  The kernel orders every fragment read
+// after the copies into its stage with its own vmcnt waits and that barrier.
+// The stages are separate LDS arrays and the loop is unrolled by 5, so every
+// fragment address in the steady loop is a constant stage base plus one
+// per-lane offset.
 //
 // Software pipeline.  Step j of a wave interleaves, in one instruction
 // stream, the matrix products of two neighbouring tiles with the vector work
@@ -261,8 +263,9 @@ struct Layout {
     static constexpr int BLOCKS = ELEMS / 512;   // 1 KiB DMA blocks per tensor
     static constexpr int STAGE = 2 * ELEMS;  // K + V
     static constexpr int DPW = 2 * BLOCKS / WAVES;   // DMA blocks per wave
-    // merge area: per wave its accumulators (ACC floats per lane), then the
-    // (m, l, lr) of both row blocks of every wave
+    // merge area: per wave room for its accumulators (ACC floats per lane;
+    // the merge publishes one row block of them), then the (m, l, lr) of
+    // both row blocks of every wave
     static constexpr int ACC = 2 * NDB * 16;
     static constexpr int SLOTS_PER_STAGE = (STAGE * 2) / (ACC * 64 * 4);
     static_assert(SLOTS_PER_STAGE >= 1, "merge slot fits a stage");
@@ -271,8 +274,8 @@ struct Layout {
     static_assert(kStages * STAGE * 2 * WG_PER_CU <= 160 * 1024, "LDS per CU");
 };
 
-// Stage K of the LDS ring of a work-group (one array per stage, so that the
-// compiler tells a stage being read apart from one a copy is landing in).
+// Stage K of the LDS ring of a work-group (one array per stage: in the
+// unrolled loop every stage address is a compile-time constant).
 template <int D, int K>
 __device__ __forceinline__ lds16_t* ring() {
     __shared__ __attribute__((aligned(16))) uint16_t r[Layout<D>::STAGE];
@@ -481,7 +484,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         m[rb] = -__builtin_inff();
         nm[rb] = 0.0f;
         l[rb] = 0.0f;
-        lr[rb] = 0.0f;                   // sum of the rounded P
+        lr[rb] = 0.0f;                   // sum of the rounded P (bf16)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x16_t{};
     }
@@ -502,9 +505,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     }
 
     // Per-lane element offsets of the wave's fragments in a stage, opaque to
-    // the optimiser: every fragment address is then one stage array plus one
-    // variable index plus a constant, a form whose stage the compiler can
-    // still tell apart from the stages copies are landing in.
+    // the optimiser (re-pinned after every step's barrier): every fragment
+    // address is one stage array plus one variable index plus a constant,
+    // and no fragment read can be hoisted above the barrier that makes its
+    // stage's copies visible.
     int k_off = (kq * NKS) * 512 + lane * 8;
     int v_off = L::ELEMS + (2 * kq) * 512 + lane * 4;
     asm volatile("" : "+v"(k_off));
