@@ -17,10 +17,10 @@
 // are exponentiated against it without computing their max (any reference
 // gives the same O = u / l and LSE = m + log2 l, and every row's largest
 // probability is at least 1, so none underflows to a zero sum).  Only an
-// overflow is wrong: a probability past the 16-bit range leaves a lane's fp32
-// row sum at or above that range's maximum, and the work-group then redoes
-// the q-tile in a safe form that moves a row's reference whenever a tile's
-// max exceeds it by more than 2^8.  The row sums are taken in fp32 from the
+// overflow is wrong: when a probability passes the 16-bit range (seen as an
+// inf or NaN accumulator for fp16, as an fp32 row sum past the largest bf16
+// for bf16), the work-group redoes the q-tile in a safe form that moves a
+// row's reference whenever a tile's max exceeds it by more than 2^8.  The row sums are taken in fp32 from the
 // unrounded probabilities.  For fp16 inputs they also normalise the output
 // (rounding P to fp16 moves the product by at most 2^-11 relative); for bf16
 // inputs the output is normalised by the sum of the probabilities as rounded
@@ -110,10 +110,10 @@ template <> struct Mma<f16_t> {
             0, 0, 0);
     }
     // O is normalised by the fp32 row sum: fp16 rounding of P moves the
-    // product by at most 2^-11 relative.  A P past the fp16 range can only
-    // occur in a lane whose fp32 sum reaches kPMax, which sends the q-tile to
-    // the safe form.  (The sum of the rounded P would cost one v_dot2 per
-    // pair, and those do not overlap the matrix products.)
+    // product by at most 2^-11 relative.  A P past the fp16 range turns into
+    // inf in the P operand; the non-finite accumulators it leaves send the
+    // q-tile to the safe form.  (The sum of the rounded P would cost one
+    // v_dot2 per pair, and those do not overlap the matrix products.)
     static constexpr bool kNormRounded = false;
     static constexpr float kPMax = 65504.0f;
     __device__ __forceinline__ static float add_pair(uint32_t pr, float c) {
@@ -972,10 +972,25 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         };
         if (kq == 0) put(I1());
         else put(I0());
-        // a probability past the 16-bit range (or an inf / NaN) leaves some
-        // lane's fp32 sum at or above kPMax
-        const bool bad = __builtin_amdgcn_ballot_w64(
-                             !(l[0] < Mma<Tin>::kPMax && l[1] < Mma<Tin>::kPMax)) != 0;
+        // A probability past the 16-bit range: for bf16 it leaves some lane's
+        // fp32 sum at or above kPMax.  For fp16 it becomes inf in the P
+        // operand and leaves an inf or NaN in the accumulators: sum(acc * 0)
+        // is NaN exactly then (a long row of moderate probabilities can pass
+        // 65504 in the fp32 sum without any single one overflowing).
+        bool ok = l[0] + l[1] < __builtin_inff();
+        if constexpr (Mma<Tin>::kNormRounded) {
+            ok = ok && l[0] < Mma<Tin>::kPMax && l[1] < Mma<Tin>::kPMax;
+        } else {
+            float z = 0.0f;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) z = fmaf(acc[rb][db][i], 0.0f, z);
+            ok = ok && z == 0.0f;
+        }
+        const bool bad = __builtin_amdgcn_ballot_w64(!ok) != 0;
         if (lane == 0) *ovf_flag(wave) = bad ? 1.0f : 0.0f;
         __syncthreads();
     };

@@ -336,6 +336,17 @@ def test_reference_jump(d, causal, dtype, boost):
     note(f"  err_O {eo:.3e}  err_LSE {el:.3e}")
 
 
+def test_long_row_with_large_fp16_sums():
+    """fp16, 300000 keys with near-uniform scores: every lane's fp32 row sum
+    passes 65504 while no probability leaves the fp16 range."""
+    note("long row, large fp16 sums")
+    q, k, v = workloads.make_dense(1, 1, 1, 64, 300000, 64, F16, seed=5)
+    o, lse = run_gpu(q, k, v, scale=1e-3)
+    o_ref, l_ref = oracle.attention(workloads.to_f64(q), workloads.to_f64(k),
+                                    workloads.to_f64(v), scale=1e-3)
+    compare(o, lse, o_ref, l_ref)
+
+
 def test_permutation_invariance():
     note("permutation invariance")
     q, k, v = workloads.make_dense(1, 2, 2, 130, 250, 64, BF16, seed=11)
