@@ -1146,10 +1146,11 @@ template <int D, typename Tin, typename Tout>
 hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
     const int n_qtiles = (p.lq + kBM - 1) / kBM;
     // causal q-tile order: with two resident work-groups per CU, grid
-    // halves heaviest-first and lightest-first; with one, q-tile pairs
+    // halves heaviest-first and lightest-first (2); with one, heaviest first
+    // (0: measured 1 % faster than q-tile pairs in one work-group at d = 128)
     const int pair = !p.causal ? 0
                      : p.causal_pairs >= 0 ? p.causal_pairs
-                     : (Layout<D>::WG_PER_CU == 2 ? 2 : 1);
+                     : (Layout<D>::WG_PER_CU == 2 ? 2 : 0);
     const int items = (p.causal && pair == 1) ? (n_qtiles + 1) / 2 : n_qtiles;
     // grid limits (y and z below 2^16) are checked by the caller
     const dim3 grid((unsigned)p.hq, (unsigned)p.batch, (unsigned)items);
