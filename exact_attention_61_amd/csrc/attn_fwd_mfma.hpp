@@ -616,7 +616,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             if (next) {
 #pragma unroll
                 for (int t = 0; t < DPW; ++t)
-                    if (gi == 2 + t * (kGroups - 3) / DPW) issue_part(rsrc, dma_stage, t);
+                    if (gi == 3 + t * (kGroups - 4) / DPW) issue_part(rsrc, dma_stage, t);
             }
         };
         const auto rsrc = tile_rsrc(dma_kt);
