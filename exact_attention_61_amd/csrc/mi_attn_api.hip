@@ -32,11 +32,8 @@ bool stride_ok(const mi_attn_strides_t& s) {
 // MI_ATTN_KERNEL=simple selects the scalar kernel (a second, independent
 // implementation kept for cross-checks); anything else runs the MFMA kernel.
 bool use_scalar_kernel() {
-    static const bool v = [] {
-        const char* e = std::getenv("MI_ATTN_KERNEL");
-        return e != nullptr && std::strcmp(e, "simple") == 0;
-    }();
-    return v;
+    const char* e = std::getenv("MI_ATTN_KERNEL");   // read on every call
+    return e != nullptr && std::strcmp(e, "simple") == 0;
 }
 
 // Causal q-tile order of the MFMA kernel (MI_ATTN_CAUSAL_PAIRS): 0 = one

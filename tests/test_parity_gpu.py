@@ -347,6 +347,34 @@ def test_long_row_with_large_fp16_sums():
     compare(o, lse, o_ref, l_ref)
 
 
+# The scalar reference kernel (MI_ATTN_KERNEL=simple): a second, independent
+# HIP implementation, checked against the oracle on its own.
+@pytest.mark.parametrize("b,hq,hkv,lq,lk,d,dtype,causal", [
+    (1, 2, 2, 130, 250, 64, BF16, False),
+    (2, 4, 2, 200, 200, 64, F16, True),
+    (1, 6, 3, 129, 300, 128, BF16, True),
+    (1, 2, 1, 300, 129, 128, F16, True),     # fewer keys: early rows see none
+])
+def test_scalar_kernel(monkeypatch, b, hq, hkv, lq, lk, d, dtype, causal):
+    monkeypatch.setenv("MI_ATTN_KERNEL", "simple")
+    note(f"scalar kernel b{b} hq{hq} hkv{hkv} lq{lq} lk{lk} d{d} {dtype} causal {causal}")
+    dense_case(b, hq, hkv, lq, lk, d, dtype, causal)
+
+
+def test_scalar_kernel_varlen(monkeypatch):
+    monkeypatch.setenv("MI_ATTN_KERNEL", "simple")
+    lens_q = [5, 130, 0, 77]
+    lens_k = [9, 130, 4, 0]
+    note(f"scalar kernel varlen lens_q {lens_q} lens_k {lens_k}")
+    q, k, v, cq, ck = workloads.make_packed(lens_q, lens_k, 4, 2, 64, BF16, seed=3)
+    o, lse = run_gpu(q, k, v, cu_seqlens_q=cq, cu_seqlens_k=ck,
+                     max_seqlen_q=max(lens_q), max_seqlen_k=max(lens_k), causal=True)
+    f64 = workloads.to_f64
+    o_ref, l_ref = oracle.attention(f64(q), f64(k), f64(v), causal=True,
+                                    cu_seqlens_q=cq.numpy(), cu_seqlens_k=ck.numpy())
+    compare(o, lse, o_ref, l_ref)
+
+
 def test_permutation_invariance():
     note("permutation invariance")
     q, k, v = workloads.make_dense(1, 2, 2, 130, 250, 64, BF16, seed=11)
