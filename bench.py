@@ -4,18 +4,31 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one forward pass (one kernel launch) over the whole workload, with
-Q, K, V and the outputs resident in HBM.  The K timed steps are captured
-back-to-back in one HIP graph and replayed between two HIP events recorded
-on the stream the kernels run on, so launch overhead on the host is not in
-the figure; `ms_per_step_eager` gives the plain per-call rate for context.
+Q, K, V and the outputs resident in HBM.  The K timed steps run as 5 batches
+of back-to-back launches (each batch one HIP graph replay), with a HIP event
+recorded on the launch stream before the first batch and after every batch:
+the timed region is exactly the K steps, `ms_per_step` is its total over K,
+and `ms_per_step_median_batch` the median of the 5 batches' per-launch
+times.  Host launch overhead is not in the figures; `ms_per_step_eager`
+gives the plain per-call rate for context.
 
 Prints one JSON line.  `value` is algorithmic TFLOP/s of the workload:
 4 * d * Hq * (visible query/key pairs) per forward.  `roofline` relates the
-kernel to the dense fp16/bf16 MFMA peak of MI355X; `traffic` comes from
-rocprofv3 counters committed under profiles/ and is reported only while the
-kernel source still hashes to the value recorded with them.  `cpu_baseline`
-times the fp64 CPU oracle on the host cores over the same workload and also
-yields the parity errors of this run's GPU output.
+kernel to the dense fp16/bf16 MFMA peak of MI355X; `traffic` (HBM bytes per
+launch) and `mfma_busy` come from rocprofv3 counters committed under
+profiles/ and are reported only while the kernel source still hashes to the
+value recorded with them.  `cpu_baseline` times the fp64 CPU oracle on the
+host cores over the same workload and also yields the parity errors of this
+run's GPU output.  `memory` compares torch's peak allocation during the
+calls with the inputs and outputs (the library allocates nothing, so no
+Lq x Lk buffer can exist).
+
+    python bench.py --summarize-counters DIR [--workload NAME] [--write-record]
+
+reads the CSV files of the rocprofv3 runs listed in the summary it prints
+(kernel trace, HBM read and write request counters, MFMA busy cycles) from
+DIR and prints a Markdown summary; --write-record also stores the per-launch
+figures in the counter record under profiles/.
 """
 
 import argparse
@@ -35,7 +48,10 @@ KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_61_amd", *parts) for parts in
                (("csrc", "attn_fwd_mfma.hpp"), ("csrc", "attn_fwd_mfma_d64.hip"),
                 ("csrc", "attn_fwd_mfma_d128.hip"), ("csrc", "common.hpp"),
                 ("build.py",))]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_mfma_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_mfma_counters.json")
+# What the headline line is quoted on (the workload's own label otherwise).
+HEADLINE_METRIC = ("attn fwd TFLOP/s + % of fp16 MFMA peak, B2 H16 N2048 d64 "
+                   "causal")
 
 
 def visible_pairs(w, lengths=None):
@@ -69,8 +85,9 @@ def kernel_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload):
-    """HBM bytes per launch from the committed counter summary, or None."""
+def load_counter_record(workload):
+    """Per-launch counter figures of the workload from the committed record,
+    or None when there is none or the kernel has changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -78,10 +95,30 @@ def load_traffic(workload):
         return None
     if rec.get("kernel_sha256_16") != kernel_hash():
         return None
-    ent = rec.get("workloads", {}).get(workload)
-    if not ent:
-        return None
-    return ent.get("hbm_bytes_per_launch")
+    return rec.get("workloads", {}).get(workload) or None
+
+
+def load_traffic(workload):
+    """HBM bytes per launch from the committed counter record, or None."""
+    ent = load_counter_record(workload)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def metric_label(w):
+    """The metric string of a workload's line."""
+    import workloads
+    if w.name == workloads.HEADLINE:
+        return HEADLINE_METRIC
+    shape = (f"varlen B{w.batch} H{w.hq} max L{w.lq}" if w.varlen else
+             f"B{w.batch} Hq{w.hq} Hkv{w.hkv} Lq{w.lq} Lk{w.lk}")
+    return (f"attn fwd TFLOP/s + % of {w.in_dtype} MFMA peak, {shape} d{w.d}"
+            f"{' causal' if w.causal else ''}")
+
+
+def batch_sizes(steps, batches=5):
+    """Split `steps` launches into at most `batches` nearly equal batches."""
+    nb = max(1, min(batches, steps))
+    return [steps // nb + (1 if i < steps % nb else 0) for i in range(nb)]
 
 
 def blas_threads():
@@ -130,6 +167,119 @@ def cpu_baseline(w, inp, o_gpu, lse_gpu, flops, min_seconds=10.0):
     return base, parity
 
 
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath, suffix):
+    for root, _, files in os.walk(dirpath):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+
+
+def _per_dispatch(path, kernel_sub):
+    """Counter values per dispatch of the kernel: {counter: [values]}."""
+    per = {}
+    for r in _csv_rows(path):
+        if kernel_sub not in r["Kernel_Name"]:
+            continue
+        key = (r["Dispatch_Id"], r["Counter_Name"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (_, name), val in per.items():
+        out.setdefault(name, []).append(val)
+    return out
+
+
+def summarize_counters(dirpath, name, write_record):
+    """Markdown summary of the rocprofv3 runs of one workload (see the
+    commands it prints) and, optionally, the committed counter record."""
+    import statistics
+    import workloads
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make(name, seed=0)
+    flops = 4.0 * w.d * w.hq * visible_pairs(w, inp.get("lengths"))
+    nbytes = algorithmic_bytes(w, inp)
+    kern = "attn_fwd_mfma_kernel"
+    wl = f"--workload {name} "
+    cmds = {
+        "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o t -- python3 bench.py {wl}--steps 50 --warmup 5 --no-cpu-baseline",
+        "read": f"rocprofv3 --pmc TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum TCC_EA0_RDREQ_sum --output-format csv -d DIR/read -o r -- python3 bench.py {wl}--steps 5 --warmup 2 --no-cpu-baseline",
+        "write": f"rocprofv3 --pmc TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum --output-format csv -d DIR/write -o w -- python3 bench.py {wl}--steps 5 --warmup 2 --no-cpu-baseline",
+        "mfma": f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES --output-format csv -d DIR/mfma -o m -- python3 bench.py {wl}--steps 5 --warmup 2 --no-cpu-baseline",
+    }
+    tr = [r for r in _csv_rows(_find(os.path.join(dirpath, "trace"), "kernel_trace.csv"))
+          if kern in r["Kernel_Name"]]
+    dur = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr]
+    t_avg = statistics.mean(dur) * 1e-9
+    rd = _per_dispatch(_find(os.path.join(dirpath, "read"), "counter_collection.csv"), kern)
+    wr = _per_dispatch(_find(os.path.join(dirpath, "write"), "counter_collection.csv"), kern)
+    mf = _per_dispatch(_find(os.path.join(dirpath, "mfma"), "counter_collection.csv"), kern)
+    m = lambda d, k: statistics.mean(d[k])
+    n32, n64, n128 = (m(rd, f"TCC_EA0_RDREQ_{x}B_sum") for x in (32, 64, 128))
+    nall = m(rd, "TCC_EA0_RDREQ_sum")
+    read_b = 32 * n32 + 64 * n64 + 128 * n128
+    w_all, w64 = m(wr, "TCC_EA0_WRREQ_sum"), m(wr, "TCC_EA0_WRREQ_64B_sum")
+    write_b = 64 * w64 + 32 * (w_all - w64)
+    busy = m(mf, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = m(mf, "GRBM_GUI_ACTIVE")
+    mops = m(mf, "SQ_INSTS_VALU_MFMA_MOPS_F16") + m(mf, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    simds = 4 * 256
+    util_gui = busy / (gui * simds)
+    exec_flops = mops * 512
+    h = kernel_hash()
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    in_b = (q.numel() + k.numel() + v.numel()) * 2
+    lines = [
+        f"# {kern} — {name} — kernel trace, HBM bytes and MFMA counters", "",
+        f"Workload: {metric_label(w)}; {flops / 1e9:.3f} GFLOP algorithmic per launch, "
+        f"{nbytes} algorithmic bytes (Q+K+V read once, O+LSE written once).", "",
+        "Commands (repository root, MI355X, `TMPDIR=/tmp`, library built by "
+        "`python exact_attention_61_amd/build.py`; each counter pass its own run):", "",
+        *[f"    {c}" for c in cmds.values()],
+        f"    python bench.py --summarize-counters DIR --workload {name}", "",
+        "| quantity | per launch |", "|---|---|",
+        f"| kernel duration (trace, {len(dur)} dispatches) | mean {t_avg * 1e6:.2f} us, median "
+        f"{statistics.median(dur) / 1e3:.2f} us, min {min(dur) / 1e3:.2f} us |",
+        f"| algorithmic TFLOP/s at the mean duration | {flops / t_avg / 1e12:.1f} "
+        f"({100 * flops / t_avg / 1e12 / PEAK_TFLOPS[w.in_dtype]:.2f} % of {PEAK_TFLOPS[w.in_dtype]}) |",
+        f"| read requests 32 B / 64 B / 128 B (all) | {n32:.0f} / {n64:.0f} / {n128:.0f} ({nall:.0f}) |",
+        f"| HBM read bytes (32·n32 + 64·n64 + 128·n128) | {read_b / 2**20:.2f} MiB = "
+        f"{read_b / in_b:.3f} x Q+K+V ({in_b / 2**20:.2f} MiB) |",
+        f"| write requests (64 B of them) | {w_all:.0f} ({w64:.0f}) |",
+        f"| HBM write bytes | {write_b / 2**20:.2f} MiB = {write_b / (nbytes - in_b):.3f} x O+LSE "
+        f"({(nbytes - in_b) / 2**20:.2f} MiB) |",
+        f"| MFMA busy cycles / (GRBM_GUI_ACTIVE x {simds} SIMDs) | {100 * util_gui:.1f} % |",
+        f"| executed MFMA flops (MOPS x 512) | {exec_flops / 1e9:.3f} GFLOP = "
+        f"{exec_flops / flops:.3f} x algorithmic |", "",
+        f"Kernel source sha256[:16] = {h}.",
+    ]
+    print("\n".join(lines))
+    if write_record:
+        try:
+            with open(TRAFFIC_FILE) as f:
+                rec = json.load(f)
+        except (OSError, ValueError):
+            rec = {}
+        if rec.get("kernel_sha256_16") != h:
+            rec = {"kernel_sha256_16": h, "workloads": {}}
+        rec["workloads"][name] = {
+            "hbm_bytes_per_launch": int(round(read_b + write_b)),
+            "hbm_read_bytes_per_launch": int(round(read_b)),
+            "hbm_write_bytes_per_launch": int(round(write_b)),
+            "mfma_busy": round(util_gui, 4),
+            "kernel_us_mean": round(t_avg * 1e6, 3),
+            "executed_mfma_flops": exec_flops,
+            "source": f"profiles/{kern}_{name}_counters.md"}
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +290,12 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB "
                          "(reference point for the HBM byte counters)")
+    ap.add_argument("--summarize-counters", default=None, metavar="DIR",
+                    help="print the Markdown summary of the rocprofv3 runs "
+                         "under DIR (no GPU work)")
+    ap.add_argument("--write-record", action="store_true",
+                    help="with --summarize-counters: update the counter "
+                         "record under profiles/")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): "
@@ -147,6 +303,15 @@ def main():
               "with no exchange, and no multi-GPU figure is produced.",
               file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1:
+        print("--steps must be at least 1", file=sys.stderr)
+        sys.exit(2)
+    if args.summarize_counters:
+        import workloads
+        summarize_counters(args.summarize_counters,
+                           args.workload or workloads.HEADLINE,
+                           args.write_record)
+        return
 
     import torch
     if args.copy_calibration:
@@ -188,33 +353,48 @@ def main():
     flops = 4.0 * w.d * w.hq * visible_pairs(w, lengths)
     nbytes = algorithmic_bytes(w, inp)
 
-    # warm-up (eager), then capture K back-to-back launches in one graph
+    # warm-up (eager), with torch's peak-allocation counter reset first:
+    # everything allocated now is the inputs, outputs and cu_seqlens
+    torch.cuda.synchronize()
+    resident = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev)
+
+    # the K timed steps: batches of back-to-back launches, one graph each
+    sizes = batch_sizes(args.steps)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         step()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for _ in range(args.steps):
-            step()
-    graph.replay()                       # warm replay
+    graphs = {}
+    for n in sorted(set(sizes)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                step()
+        graphs[n] = g
+    for g in graphs.values():
+        g.replay()                       # warm replay
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sizes) + 1)]
     torch.cuda.synchronize()
-    e0.record(stream)
-    graph.replay()
-    e1.record(stream)
+    ev[0].record(stream)
+    for i, n in enumerate(sizes):
+        graphs[n].replay()
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
+    ms_total = ev[0].elapsed_time(ev[-1])
     ms = ms_total / args.steps
+    per_batch = sorted(ev[i].elapsed_time(ev[i + 1]) / n
+                       for i, n in enumerate(sizes))
+    ms_median = per_batch[len(per_batch) // 2]
 
     # plain eager calls, for context
     torch.cuda.synchronize()
@@ -225,9 +405,9 @@ def main():
     ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
 
     tflops = flops / (ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.in_dtype]
+    peak_tf = PEAK_TFLOPS[w.in_dtype]
     props = torch.cuda.get_device_properties(dev)
-    traffic = load_traffic(name)
+    counters = load_counter_record(name)
 
     o_gpu = o.to("cpu", torch.float64).numpy()
     lse_gpu = lse.to("cpu", torch.float64).numpy()
@@ -236,8 +416,7 @@ def main():
         base, parity = cpu_baseline(w, inp, o_gpu, lse_gpu, flops)
 
     rec = {
-        "metric": "attn fwd TFLOP/s + % of fp16 MFMA peak, B2 H16 N2048 d64 "
-                  "causal",
+        "metric": metric_label(w),
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -254,18 +433,24 @@ def main():
                    "causal": w.causal, "varlen": w.varlen,
                    "in_dtype": w.in_dtype, "out_dtype": w.out_dtype,
                    "lengths": lengths},
-        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "pct_of_peak": round(100.0 * tflops / peak_tf, 2),
         "algorithmic_flops": flops,
         # the common convention: 4*B*H*Lq*Lk*d, halved for causal
         "flops_common_convention": (2.0 if w.causal else 4.0) * w.batch *
         w.hq * w.lq * w.lk * w.d,
+        "ms_per_step_median_batch": round(ms_median, 6),
+        "batches": sizes,
         "ms_per_step_eager": round(ms_eager, 6),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
-                     "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4),
-                     "traffic": traffic,
+                     "peak": peak_tf, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak_tf, 4),
+                     "traffic": None if counters is None else counters.get("hbm_bytes_per_launch"),
+                     "mfma_busy": None if counters is None else counters.get("mfma_busy"),
                      "algorithmic_bytes": nbytes,
                      "kernel": "attn_fwd_mfma_kernel"},
+        "memory": {"peak_allocated_bytes": int(peak),
+                   "inputs_outputs_bytes": int(resident),
+                   "ratio": round(peak / resident, 4) if resident else None},
         "cpu_baseline": base,
         "parity": parity,
         "device": {"name": props.name, "cus": props.multi_processor_count,

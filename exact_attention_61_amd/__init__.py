@@ -7,6 +7,8 @@ shared library has not been built, importing this package raises.
 Entry points mirror the C ABI of include/mi_attn.h:
 
 * mi_attn_fwd(q, k, v, o, lse, ...)  -- writes into caller-provided tensors;
+* mi_attn_fwd_select(..., kernel=, causal_order=) -- the same with the kernel
+  and the causal tile order chosen explicitly (tests and diagnostics);
 * mi_attn_status_string(code), mi_attn_version(), mi_attn_last_hip_error();
 
 plus forward(q, k, v, ...) -> (out, lse), which allocates the outputs.
@@ -22,6 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmi_attn.so")
 
 MI_ATTN_F16, MI_ATTN_BF16, MI_ATTN_F32 = 0, 1, 2
+MI_ATTN_KERNEL_MFMA, MI_ATTN_KERNEL_SCALAR = 0, 1
 _DTYPE_CODE = {torch.float16: MI_ATTN_F16, torch.bfloat16: MI_ATTN_BF16,
                torch.float32: MI_ATTN_F32}
 
@@ -49,8 +52,9 @@ class MiAttnError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"libmi_attn.so is not built ({LIB_PATH} missing); run "
-            "`python -m exact_attention_61_amd.build` first")
+            f"libmi_attn.so is not built ({LIB_PATH} missing); build it with "
+            "`python exact_attention_61_amd/build.py` from the repository "
+            "root (or __graft_entry__.build())")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     S = ctypes.POINTER(Strides)
@@ -59,6 +63,8 @@ def _load():
     lib.mi_attn_fwd.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int,
                                 i32, i32, i32, i32, i32, i32, S, S, S, S, P, P,
                                 ctypes.c_float, i32, P]
+    lib.mi_attn_fwd_select.restype = ctypes.c_int
+    lib.mi_attn_fwd_select.argtypes = lib.mi_attn_fwd.argtypes + [ctypes.c_int, i32]
     lib.mi_attn_status_string.restype = ctypes.c_char_p
     lib.mi_attn_status_string.argtypes = [ctypes.c_int]
     lib.mi_attn_version.restype = i32
@@ -126,6 +132,23 @@ def mi_attn_fwd(q, k, v, o, lse=None, *, causal=False, scale=None,
     max_seqlen_q / max_seqlen_k.  lse (float32) is [B, Hq, Lq] dense or
     [Hq, Tq] packed, or None.  scale=None means 1/sqrt(head_dim).
     """
+    _call(q, k, v, o, lse, causal, scale, cu_seqlens_q, cu_seqlens_k,
+          max_seqlen_q, max_seqlen_k, layout, stream, None)
+
+
+def mi_attn_fwd_select(q, k, v, o, lse=None, *, kernel=MI_ATTN_KERNEL_MFMA,
+                       causal_order=-1, causal=False, scale=None,
+                       cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                       max_seqlen_k=None, layout="bhsd", stream=None):
+    """mi_attn_fwd with the kernel (MI_ATTN_KERNEL_MFMA / _SCALAR) and the
+    causal q-tile order (-1 default, 0, 1, 2) chosen explicitly."""
+    _call(q, k, v, o, lse, causal, scale, cu_seqlens_q, cu_seqlens_k,
+          max_seqlen_q, max_seqlen_k, layout, stream,
+          (int(kernel), int(causal_order)))
+
+
+def _call(q, k, v, o, lse, causal, scale, cu_seqlens_q, cu_seqlens_k,
+          max_seqlen_q, max_seqlen_k, layout, stream, select):
     packed = cu_seqlens_q is not None or cu_seqlens_k is not None
     for t in (q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k):
         if t is not None and (not t.is_cuda or t.device != q.device):
@@ -156,13 +179,16 @@ def mi_attn_fwd(q, k, v, o, lse=None, *, causal=False, scale=None,
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     qs, ks, vs, os_ = (_strides(t, layout, packed) for t in (q, k, v, o))
-    st = _lib.mi_attn_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-        _DTYPE_CODE[q.dtype], _DTYPE_CODE[o.dtype],
-        bsz, hq, hkv, lq, lk, d,
-        ctypes.byref(qs), ctypes.byref(ks), ctypes.byref(vs),
-        ctypes.byref(os_), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
-        float(scale), int(bool(causal)), ctypes.c_void_p(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+            _DTYPE_CODE[q.dtype], _DTYPE_CODE[o.dtype],
+            bsz, hq, hkv, lq, lk, d,
+            ctypes.byref(qs), ctypes.byref(ks), ctypes.byref(vs),
+            ctypes.byref(os_), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+            float(scale), int(bool(causal)), ctypes.c_void_p(stream))
+    if select is None:
+        st = _lib.mi_attn_fwd(*args)
+    else:
+        st = _lib.mi_attn_fwd_select(*args, *select)
     if st != 0:
         detail = ""
         if st == 7:
@@ -185,8 +211,12 @@ def _check_cu(cu, max_len, rows):
 
 def forward(q, k, v, *, causal=False, scale=None, cu_seqlens_q=None,
             cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-            out_dtype=None, layout="bhsd", return_lse=True):
-    """Allocate out (and lse) and run mi_attn_fwd; returns (out, lse)."""
+            out_dtype=None, layout="bhsd", return_lse=True, kernel=None,
+            causal_order=None):
+    """Allocate out (and lse) and run mi_attn_fwd; returns (out, lse).
+
+    kernel / causal_order (optional) go through mi_attn_fwd_select instead.
+    """
     packed = cu_seqlens_q is not None or cu_seqlens_k is not None
     out_dtype = q.dtype if out_dtype is None else out_dtype
     out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
@@ -199,9 +229,16 @@ def forward(q, k, v, *, causal=False, scale=None, cu_seqlens_q=None,
             bsz, hq, _, lq, _ = _dims(q, k, layout, packed)
             lse = torch.empty((bsz, hq, lq), dtype=torch.float32,
                               device=q.device)
+    kw = dict(causal=causal, scale=scale, cu_seqlens_q=cu_seqlens_q,
+              cu_seqlens_k=cu_seqlens_k, max_seqlen_q=max_seqlen_q,
+              max_seqlen_k=max_seqlen_k, layout=layout)
     with torch.cuda.device(q.device):
-        mi_attn_fwd(q, k, v, out, lse, causal=causal, scale=scale,
-                    cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
-                    max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
-                    layout=layout)
+        if kernel is None and causal_order is None:
+            mi_attn_fwd(q, k, v, out, lse, **kw)
+        else:
+            mi_attn_fwd_select(
+                q, k, v, out, lse,
+                kernel=MI_ATTN_KERNEL_MFMA if kernel is None else kernel,
+                causal_order=-1 if causal_order is None else causal_order,
+                **kw)
     return out, lse

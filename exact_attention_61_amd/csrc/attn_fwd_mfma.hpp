@@ -102,6 +102,23 @@ template <typename T> struct Mma;
 // max exceeds it by more than this (log2 units).
 constexpr float kGap = 8.0f;
 
+// P is rounded to the input type for the PV product; the log-sum-exp always
+// uses the fp32 sum of the unrounded probabilities.
+//
+// fp16 keeps 11 significant bits: O is normalised by the same fp32 sum, and
+// the rounding of P moves the product by at most 2^-11 relative.
+//
+// bf16 keeps 8, too coarse on its own in two situations.  (1) One key
+// dominates a row from a tile after the first: its probability, rounded,
+// would carry ~2^-9 relative error into O.  O is therefore normalised by the
+// sum of the probabilities as rounded (kNormRounded, one v_dot2 per pair),
+// so the rounding of a dominant probability cancels between numerator and
+// denominator.  (2) A row sees only a few keys: then each rounded
+// probability moves O by up to ~2^-9 of a value, on top of the output's own
+// bf16 rounding.  Every row with fewer than BN visible keys has all of them
+// in the masked tiles at the end of its range, so on those tiles (and only
+// there) bf16 splits P into hi = bf16(p) and lo = bf16(p - hi) and runs the
+// PV product twice (kSplit); hi + lo carries 16 significant bits.
 template <> struct Mma<f16_t> {
     __device__ __forceinline__ static f32x16_t run(u32x4_t a, u32x4_t b,
                                                    f32x16_t c) {
@@ -109,17 +126,11 @@ template <> struct Mma<f16_t> {
             __builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
             0, 0, 0);
     }
-    // O is normalised by the fp32 row sum: fp16 rounding of P moves the
-    // product by at most 2^-11 relative.  A P past the fp16 range turns into
-    // inf in the P operand; the non-finite accumulators it leaves send the
-    // q-tile to the safe form.  (The sum of the rounded P would cost one
-    // v_dot2 per pair, and those do not overlap the matrix products.)
+    static constexpr bool kSplit = false;
     static constexpr bool kNormRounded = false;
-    static constexpr float kPMax = 65504.0f;
     __device__ __forceinline__ static float add_pair(uint32_t pr, float c) {
         const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pr), one, c,
-                                      false);
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pr), one, c, false);
     }
     // two fp32 -> packed 16-bit, round to nearest even (v_cvt_pk_f16_f32)
     __device__ __forceinline__ static uint32_t pack(float x, float y) {
@@ -127,6 +138,12 @@ template <> struct Mma<f16_t> {
         r[0] = (_Float16)x;
         r[1] = (_Float16)y;
         return __builtin_bit_cast(uint32_t, r);
+    }
+    __device__ __forceinline__ static float lo16(uint32_t p) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)p);
+    }
+    __device__ __forceinline__ static float hi16(uint32_t p) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
     }
 };
 template <> struct Mma<bf16_t> {
@@ -136,17 +153,12 @@ template <> struct Mma<bf16_t> {
             __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
             c, 0, 0, 0);
     }
-    // bf16 rounding is too coarse for the log-sum-exp: it uses the fp32
-    // sum, and O is normalised by the sum of the rounded P (v_dot2), so the
-    // rounding of a dominant probability cancels between numerator and
-    // denominator.  kPMax stays below the largest finite bf16.
+    static constexpr bool kSplit = true;
     static constexpr bool kNormRounded = true;
-    static constexpr float kPMax = 3.0e38f;
     // c + the two packed bf16 values (exact products with 1, fp32 sum)
     __device__ __forceinline__ static float add_pair(uint32_t pr, float c) {
         const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr),
-                                               one, c, false);
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr), one, c, false);
     }
     // v_cvt_pk_bf16_f32, round to nearest even
     __device__ __forceinline__ static uint32_t pack(float x, float y) {
@@ -155,7 +167,22 @@ template <> struct Mma<bf16_t> {
         r[1] = (__bf16)y;
         return __builtin_bit_cast(uint32_t, r);
     }
+    // the two packed bf16 values back in fp32 (exact: bf16 is the upper
+    // half of an fp32)
+    __device__ __forceinline__ static float lo16(uint32_t p) {
+        return __builtin_bit_cast(float, p << 16);
+    }
+    __device__ __forceinline__ static float hi16(uint32_t p) {
+        return __builtin_bit_cast(float, p & 0xffff0000u);
+    }
 };
+// Largest per-lane row sum the short form accepts, and the largest
+// accumulator magnitude; past either the q-tile is redone in the safe form.
+// Row sums below 2^100 keep every probability far from the top of the bf16
+// and fp32 ranges, and accumulators below 2^126 keep the merge of two key
+// halves (a sum of two terms, each scaled by at most 1) finite.
+constexpr float kLMax = 1.2676506e30f;    // 2^100
+constexpr float kAccMax = 8.507059e37f;   // 2^126
 
 // Lane index 0..63 from the execution mask (all lanes active), computed anew
 // at every call: the asm is volatile, so the optimiser neither merges two
@@ -496,6 +523,15 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     f32x16_t s_cur[2];
     u32x4_t p_prev[2][2];
     u32x4_t vf[NDB][2];
+    // bf16 only: the low part of P(j-1) when tile j-1 was a masked tile,
+    // zero otherwise; only the masked steps and the last tile read it
+    u32x4_t p_lo[2][2];
+    auto clear_p_lo = [&]() {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) p_lo[rb][c] = u32x4_t{0u, 0u, 0u, 0u};
+    };
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -541,14 +577,19 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 if (8 * (e >> 2) + (e & 3) > lim) s_cur[rb][e] = -__builtin_inff();
         }
     };
-    auto pv_last = [&]() {
+    // PV of the last tile; LO: it was a masked tile, so for bf16 its P was
+    // split and the low part goes in too
+    auto pv_last = [&](auto LO) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
+                for (int rb = 0; rb < 2; ++rb) {
                     acc[rb][db] = Mma<Tin>::run(vf[db][c], p_prev[rb][c], acc[rb][db]);
+                    if constexpr (Mma<Tin>::kSplit && decltype(LO)::value)
+                        acc[rb][db] = Mma<Tin>::run(vf[db][c], p_lo[rb][c], acc[rb][db]);
+                }
     };
 
     // One pipeline step for tile j.  The matrix products of the step -- with
@@ -577,21 +618,29 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                        int dma_kt, lds16_t* dma_stage, const lds16_t* v_next) {
         constexpr bool next = decltype(NEXT)::value;
         constexpr bool safe = decltype(SAFE)::value;
+        constexpr bool masked_tile = decltype(MASK)::value;
+        // bf16 on a masked tile: this tile's P is split into hi + lo, and the
+        // PV product of the previous tile also takes its lo part (zero when
+        // that tile was not masked)
+        constexpr bool split = Mma<Tin>::kSplit && masked_tile;
         constexpr int NPV = decltype(PV)::value ? 2 * NDB * 2 : 0;
+        constexpr int NPVT = split ? 2 * NPV : NPV;   // with the lo products
         constexpr int NQK = next ? 2 * NKS : 0;
-        constexpr int NM = NPV + NQK;
+        constexpr int NM = NPVT + NQK;
         constexpr int kGroups = safe ? 13 : 9;
         // O += P(j-1) V(j-1) first: its fragments were read in the previous
         // step.  S(j+1) = Q K(j+1)^T after it, by when the K(j+1) fragments
         // read at the start of this step have landed.
         auto mfma = [&](int q) {
-            if (q < NPV) {
-                const int c = q / (2 * NDB), r2 = q % (2 * NDB);
+            if (q < NPVT) {
+                const int qp = q < NPV ? q : q - NPV;
+                const int c = qp / (2 * NDB), r2 = qp % (2 * NDB);
                 const int db = r2 / 2, rb2 = r2 % 2;
-                acc[rb2][db] = Mma<Tin>::run(vf[db][c], p_prev[rb2][c], acc[rb2][db]);
+                acc[rb2][db] = Mma<Tin>::run(vf[db][c], q < NPV ? p_prev[rb2][c] : p_lo[rb2][c],
+                                             acc[rb2][db]);
             } else if (next) {
                 // row blocks alternate: neighbouring products are independent
-                const int qq = q - NPV;
+                const int qq = q - NPVT;
                 const int rb2 = qq & 1, ks = qq >> 1;
                 s_next[rb2] = Mma<Tin>::run(kf[ks], qf[rb2][ks],
                                             ks == 0 ? f32x16_t{} : s_next[rb2]);
@@ -601,14 +650,21 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         // the one that issues the last product reading vf
         constexpr int kGroupV = [] {
             int g = 0;
-            while (NPV > 0 && (g + 1) * NM / kGroups < NPV) ++g;
-            return NPV > 0 ? g + 1 : 0;
+            while (NPVT > 0 && (g + 1) * NM / kGroups < NPVT) ++g;
+            return NPVT > 0 ? g + 1 : 0;
         }();
         auto vread_at = [&](int gi) {
             if (gi == kGroupV) read_v(v_next);
         };
-        if constexpr (decltype(MASK)::value) mask_cur(j);
+        if constexpr (masked_tile) mask_cur(j);
         u32x4_t p_new[2][2];             // this tile's P; p_prev stays for PV
+        u32x4_t p_lo_new[2][2];          // its low part (split only)
+        // pack a pair of probabilities; with the split also their low parts
+        auto pack_pair = [&](float x, float y, uint32_t& hi_out, uint32_t& lo_out) {
+            hi_out = Mma<Tin>::pack(x, y);
+            if constexpr (split)
+                lo_out = Mma<Tin>::pack(x - Mma<Tin>::lo16(hi_out), y - Mma<Tin>::hi16(hi_out));
+        };
         // The copy of tile dma_kt (NEXT only), one instruction every few
         // groups: a burst of copies from every wave at once fills the memory
         // pipeline's queue and stalls the waves behind it.
@@ -622,7 +678,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         const auto rsrc = tile_rsrc(dma_kt);
         if constexpr (!safe) {
             // Part u (0..7) = scores 4 * (u & 3) .. +3 of row block u >> 2:
-            // group g exponentiates part g and rounds and sums part g - 1.
+            // group g exponentiates and sums part g and rounds part g - 1.
             // The row sums go straight into l (fp32) and, for bf16, lr.
             float pe[2][4];              // probabilities of the last two parts
 #pragma unroll
@@ -642,15 +698,23 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 if (gi >= 1) {
                     const int u = gi - 1, rb = u >> 2, c = (u >> 1) & 1, h = u & 1;
                     const float* x = pe[u & 1];
-                    const uint32_t a = Mma<Tin>::pack(x[0], x[1]);
-                    const uint32_t d = Mma<Tin>::pack(x[2], x[3]);
+                    uint32_t a, d, alo = 0, dlo = 0;
+                    pack_pair(x[0], x[1], a, alo);
+                    pack_pair(x[2], x[3], d, dlo);
                     p_new[rb][c][2 * h] = a;
                     p_new[rb][c][2 * h + 1] = d;
-                    if (Mma<Tin>::kNormRounded) {
+                    pin(p_new[rb][c]);
+                    if constexpr (Mma<Tin>::kNormRounded) {
                         lr[rb] = Mma<Tin>::add_pair(d, Mma<Tin>::add_pair(a, lr[rb]));
+                        if constexpr (split)
+                            lr[rb] = Mma<Tin>::add_pair(dlo, Mma<Tin>::add_pair(alo, lr[rb]));
                         pin(lr[rb]);
                     }
-                    pin(p_new[rb][c]);
+                    if constexpr (split) {
+                        p_lo_new[rb][c][2 * h] = alo;
+                        p_lo_new[rb][c][2 * h + 1] = dlo;
+                        pin(p_lo_new[rb][c]);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -717,15 +781,20 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int e = 8 * c + 2 * jj;
-                        p_new[rb][c][jj] = Mma<Tin>::pack(s_cur[rb][e], s_cur[rb][e + 1]);
-                        if (Mma<Tin>::kNormRounded) {
-                            if (jj & 1) t1 = Mma<Tin>::add_pair(p_new[rb][c][jj], t1);
-                            else t0 = Mma<Tin>::add_pair(p_new[rb][c][jj], t0);
+                        uint32_t hv, lv = 0;
+                        pack_pair(s_cur[rb][e], s_cur[rb][e + 1], hv, lv);
+                        p_new[rb][c][jj] = hv;
+                        if constexpr (split) p_lo_new[rb][c][jj] = lv;
+                        if constexpr (Mma<Tin>::kNormRounded) {
+                            float& t = (jj & 1) ? t1 : t0;
+                            t = Mma<Tin>::add_pair(hv, t);
+                            if constexpr (split) t = Mma<Tin>::add_pair(lv, t);
                         }
                     }
                     rsr[rb][c] = t0 + t1;
                     pin(p_new[rb][c]);
                     pin(rsr[rb][c]);
+                    if constexpr (split) pin(p_lo_new[rb][c]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -737,7 +806,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
                 l[rb] += (psum[rb][0] + psum[rb][1]) + (psum[rb][2] + psum[rb][3]);
-                if (Mma<Tin>::kNormRounded) lr[rb] += rsr[rb][0] + rsr[rb][1];
+                if constexpr (Mma<Tin>::kNormRounded) lr[rb] += rsr[rb][0] + rsr[rb][1];
             }
             // the accumulators hold P(j-1) V(j-1), relative to the old
             // references, only once this step's products are in
@@ -756,6 +825,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             for (int c = 0; c < 2; ++c) {
                 pin(p_new[rb][c]);
                 p_prev[rb][c] = p_new[rb][c];
+                if constexpr (split) p_lo[rb][c] = p_lo_new[rb][c];
             }
     };
 
@@ -900,7 +970,9 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                     }
                 }
             }
-            // masked steps up to n_kt - 2
+            // masked steps up to n_kt - 2 (the low part of P is zero for
+            // the unmasked tile before the first of them)
+            if constexpr (Mma<Tin>::kSplit) clear_p_lo();
             for (; j <= n_kt - 2; ++j) masked(j, SAFE);
             // last tile jl: no copy in flight, no product S(jl+1); then its own PV
             {
@@ -913,13 +985,15 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 f32x16_t s_unused[2];
                 // vf holds V(jl-1) (zeros if jl = 0); compute reads V(jl)
                 const lds16_t* cur = stage_of(jl);
-                if (jl >= n_full)
+                if (jl >= n_full) {
                     compute(jl, std::false_type(), std::true_type(), std::true_type(), SAFE,
                             kf_unused, s_unused, 0, ring<D, 0>(), cur);
-                else
+                    pv_last(std::true_type());
+                } else {
                     compute(jl, std::false_type(), std::true_type(), std::false_type(), SAFE,
                             kf_unused, s_unused, 0, ring<D, 0>(), cur);
-                pv_last();
+                    pv_last(std::false_type());
+                }
             }
         }
     };
@@ -951,8 +1025,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     };
     static_assert(L::WAVES * 2 * 3 * 64 + L::WAVES + 1 <= L::STAGE / 2, "flags");
     // Every wave stores the partner's row block (accumulators and
-    // statistics) and whether its short-form sums overflowed (inf or NaN:
-    // they only grow).
+    // statistics) and whether its short-form results left their range.
     auto publish = [&]() {
         __syncthreads();                 // every wave is done with the ring
         refresh_lane();
@@ -972,24 +1045,19 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         };
         if (kq == 0) put(I1());
         else put(I0());
-        // A probability past the 16-bit range: for bf16 it leaves some lane's
-        // fp32 sum at or above kPMax.  For fp16 it becomes inf in the P
-        // operand and leaves an inf or NaN in the accumulators: sum(acc * 0)
-        // is NaN exactly then (a long row of moderate probabilities can pass
-        // 65504 in the fp32 sum without any single one overflowing).
-        bool ok = l[0] + l[1] < __builtin_inff();
-        if constexpr (Mma<Tin>::kNormRounded) {
-            ok = ok && l[0] < Mma<Tin>::kPMax && l[1] < Mma<Tin>::kPMax;
-        } else {
-            float z = 0.0f;
+        // In range: every lane's row sums below kLMax and every accumulator
+        // below kAccMax in magnitude (a NaN fails both tests).  A fp16
+        // probability past 65504 is inf in the P operand, which leaves an
+        // inf or NaN accumulator; a long row of moderate probabilities may
+        // pass 65504 in its fp32 sum without any single one overflowing.
+        float amax = 0.0f;
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) z = fmaf(acc[rb][db][i], 0.0f, z);
-            ok = ok && z == 0.0f;
-        }
+                for (int i = 0; i < 16; ++i) amax = max2(amax, __builtin_fabsf(acc[rb][db][i]));
+        const bool ok = l[0] < kLMax && l[1] < kLMax && amax < kAccMax;
         const bool bad = __builtin_amdgcn_ballot_w64(!ok) != 0;
         if (lane == 0) *ovf_flag(wave) = bad ? 1.0f : 0.0f;
         __syncthreads();

@@ -7,8 +7,6 @@
 // training tutorial's constraints (Hkv divides Hq, head_dim a multiple of 8).
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
-#include <cstring>
 
 #include "../../include/mi_attn.h"
 #include "common.hpp"
@@ -29,46 +27,28 @@ bool stride_ok(const mi_attn_strides_t& s) {
            s.head % 8 == 0 && s.row % 8 == 0;
 }
 
-// MI_ATTN_KERNEL=simple selects the scalar kernel (a second, independent
-// implementation kept for cross-checks); anything else runs the MFMA kernel.
-bool use_scalar_kernel() {
-    const char* e = std::getenv("MI_ATTN_KERNEL");   // read on every call
-    return e != nullptr && std::strcmp(e, "simple") == 0;
-}
-
-// Causal q-tile order of the MFMA kernel (MI_ATTN_CAUSAL_PAIRS): 0 = one
-// q-tile per work-group, heaviest first; 1 = q-tiles t and n-1-t in one
-// work-group; 2 = one q-tile per work-group, first half of the grid heaviest
-// first and second half lightest first; unset (-1) = the kernel's default
-// for the head dimension.  Read on every call.
-int causal_pairs_setting() {
-    const char* e = std::getenv("MI_ATTN_CAUSAL_PAIRS");
-    if (e == nullptr) return -1;
-    const int x = std::atoi(e);
-    return (x >= 0 && x <= 2) ? x : -1;
-}
-
 mi_attn_strides_t default_strides(bool packed, int64_t heads, int64_t rows,
                                   int64_t d) {
     if (packed) return mi_attn_strides_t{0, d, heads * d};
     return mi_attn_strides_t{heads * rows * d, rows * d, d};
 }
 
-}  // namespace
-
-extern "C" {
-
-mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
-                             void* o, float* lse, mi_attn_dtype_t in_dtype,
-                             mi_attn_dtype_t out_dtype, int32_t batch,
-                             int32_t hq, int32_t hkv, int32_t lq, int32_t lk,
-                             int32_t head_dim, const mi_attn_strides_t* q_strides,
-                             const mi_attn_strides_t* k_strides,
-                             const mi_attn_strides_t* v_strides,
-                             const mi_attn_strides_t* o_strides,
-                             const int32_t* cu_seqlens_q,
-                             const int32_t* cu_seqlens_k, float scale,
-                             int32_t causal, struct ihipStream_t* stream) {
+// Validation and launch shared by mi_attn_fwd and mi_attn_fwd_select.
+mi_attn_status_t forward(const void* q, const void* k, const void* v,
+                         void* o, float* lse, mi_attn_dtype_t in_dtype,
+                         mi_attn_dtype_t out_dtype, int32_t batch,
+                         int32_t hq, int32_t hkv, int32_t lq, int32_t lk,
+                         int32_t head_dim, const mi_attn_strides_t* q_strides,
+                         const mi_attn_strides_t* k_strides,
+                         const mi_attn_strides_t* v_strides,
+                         const mi_attn_strides_t* o_strides,
+                         const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_k, float scale,
+                         int32_t causal, struct ihipStream_t* stream,
+                         int32_t kernel, int32_t causal_order) {
+    if (kernel != MI_ATTN_KERNEL_MFMA && kernel != MI_ATTN_KERNEL_SCALAR)
+        return MI_ATTN_ERR_ARG;
+    if (causal_order < -1 || causal_order > 2) return MI_ATTN_ERR_ARG;
     if (in_dtype != MI_ATTN_F16 && in_dtype != MI_ATTN_BF16)
         return MI_ATTN_ERR_DTYPE;
     if (out_dtype != in_dtype && out_dtype != MI_ATTN_F32)
@@ -103,6 +83,19 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
     // Q, K and V tiles are fetched with 32-bit offsets from a tile's first row.
     if (qs.row >= kMaxRowStride || ks.row >= kMaxRowStride || vs.row >= kMaxRowStride)
         return MI_ATTN_ERR_LAYOUT;
+    // Rows may not overlap: the tile copies read each row's head_dim
+    // elements from a range that ends with the last row, so a Q, K or V row
+    // stride below head_dim (for instance 0, an expanded view) would read
+    // the wrong elements, and overlapping O rows would be written by several
+    // lanes.  A tensor with a single row (dense Lq or Lk == 1) may have any
+    // row stride.
+    {
+        const bool one_q = !packed && lq == 1;
+        const bool one_k = !packed && lk <= 1;
+        if ((!one_q && (qs.row < head_dim || os.row < head_dim)) ||
+            (!one_k && (ks.row < head_dim || vs.row < head_dim)))
+            return MI_ATTN_ERR_LAYOUT;
+    }
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
         (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
         return MI_ATTN_ERR_LAYOUT;
@@ -136,11 +129,11 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
         std::fabs((double)scale) * 1.4426950408889634074, 1e-30);
     p.negate_q = scale < 0.0f ? 1 : 0;
     p.causal = causal;
-    p.causal_pairs = causal_pairs_setting();
+    p.causal_pairs = causal_order;
 
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const hipError_t err =
-        use_scalar_kernel()
+        kernel == MI_ATTN_KERNEL_SCALAR
             ? mi_attn::launch_simple(p, (int)in_dtype, (int)out_dtype,
                                      head_dim, st)
             : head_dim == 64
@@ -153,6 +146,46 @@ mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
     return MI_ATTN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
+                             void* o, float* lse, mi_attn_dtype_t in_dtype,
+                             mi_attn_dtype_t out_dtype, int32_t batch,
+                             int32_t hq, int32_t hkv, int32_t lq, int32_t lk,
+                             int32_t head_dim, const mi_attn_strides_t* q_strides,
+                             const mi_attn_strides_t* k_strides,
+                             const mi_attn_strides_t* v_strides,
+                             const mi_attn_strides_t* o_strides,
+                             const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k, float scale,
+                             int32_t causal, struct ihipStream_t* stream) {
+    return forward(q, k, v, o, lse, in_dtype, out_dtype, batch, hq, hkv, lq, lk,
+                   head_dim, q_strides, k_strides, v_strides, o_strides,
+                   cu_seqlens_q, cu_seqlens_k, scale, causal, stream,
+                   MI_ATTN_KERNEL_MFMA, -1);
+}
+
+mi_attn_status_t mi_attn_fwd_select(const void* q, const void* k, const void* v,
+                                    void* o, float* lse, mi_attn_dtype_t in_dtype,
+                                    mi_attn_dtype_t out_dtype, int32_t batch,
+                                    int32_t hq, int32_t hkv, int32_t lq, int32_t lk,
+                                    int32_t head_dim,
+                                    const mi_attn_strides_t* q_strides,
+                                    const mi_attn_strides_t* k_strides,
+                                    const mi_attn_strides_t* v_strides,
+                                    const mi_attn_strides_t* o_strides,
+                                    const int32_t* cu_seqlens_q,
+                                    const int32_t* cu_seqlens_k, float scale,
+                                    int32_t causal, struct ihipStream_t* stream,
+                                    mi_attn_kernel_t kernel, int32_t causal_order) {
+    return forward(q, k, v, o, lse, in_dtype, out_dtype, batch, hq, hkv, lq, lk,
+                   head_dim, q_strides, k_strides, v_strides, o_strides,
+                   cu_seqlens_q, cu_seqlens_k, scale, causal, stream,
+                   (int32_t)kernel, causal_order);
+}
+
 const char* mi_attn_status_string(mi_attn_status_t status) {
     switch (status) {
         case MI_ATTN_OK: return "MI_ATTN_OK: success";
@@ -161,16 +194,17 @@ const char* mi_attn_status_string(mi_attn_status_t status) {
             return "MI_ATTN_ERR_SHAPE: negative size, Hq/Hkv < 1, Hq not a "
                    "multiple of Hkv, or size beyond the launch limits";
         case MI_ATTN_ERR_LAYOUT:
-            return "MI_ATTN_ERR_LAYOUT: pointer not 16-byte aligned or stride "
-                   "negative / not a multiple of 8 elements";
+            return "MI_ATTN_ERR_LAYOUT: pointer not 16-byte aligned, stride "
+                   "negative / not a multiple of 8 elements, or a row stride "
+                   "below head_dim";
         case MI_ATTN_ERR_DTYPE:
             return "MI_ATTN_ERR_DTYPE: inputs must be F16 or BF16 and the "
                    "output the input type or F32";
         case MI_ATTN_ERR_UNSUPPORTED:
             return "MI_ATTN_ERR_UNSUPPORTED: head_dim must be 64 or 128";
         case MI_ATTN_ERR_ARG:
-            return "MI_ATTN_ERR_ARG: scale not finite, causal not 0/1, or only "
-                   "one cu_seqlens pointer given";
+            return "MI_ATTN_ERR_ARG: scale not finite, causal not 0/1, only "
+                   "one cu_seqlens pointer given, or an unknown kernel / order";
         case MI_ATTN_ERR_HIP: return "MI_ATTN_ERR_HIP: kernel launch failed";
     }
     return "unknown mi_attn status";

@@ -59,13 +59,17 @@ typedef enum mi_attn_status {
                                     Hq % Hkv != 0, Hq or B above 65535, or
                                     lq above 65535 * 128 = 8388480          */
     MI_ATTN_ERR_LAYOUT = 3,      /* pointer not 16-byte aligned, stride not a
-                                    multiple of 8 elements or negative, or a
-                                    Q/K/V row stride of 2^24 elements or more */
+                                    multiple of 8 elements or negative, a
+                                    Q/K/V row stride of 2^24 elements or more,
+                                    or a row stride below head_dim in a
+                                    tensor with more than one row            */
     MI_ATTN_ERR_DTYPE = 4,       /* in dtype not F16/BF16, or out dtype not
                                     the in dtype or F32                       */
     MI_ATTN_ERR_UNSUPPORTED = 5, /* head_dim not 64 or 128                    */
     MI_ATTN_ERR_ARG = 6,         /* scale not finite, causal not 0/1, only
-                                    one of the cu_seqlens pointers given      */
+                                    one of the cu_seqlens pointers given, or
+                                    (mi_attn_fwd_select) an unknown kernel or
+                                    causal order                              */
     MI_ATTN_ERR_HIP = 7          /* the kernel launch failed (the HIP error
                                     is kept per thread, see below)            */
 } mi_attn_status_t;
@@ -115,8 +119,10 @@ struct ihipStream_t;   /* hipStream_t; NULL is the default stream */
  * head_dim  64 or 128.
  * *_strides element strides (see mi_attn_strides_t); NULL means contiguous
  *           ([B, H, L, d] dense, [T, H, d] packed).  Strides must be >= 0 and
- *           multiples of 8, Q, K and V row strides below 2^24 elements; base
- *           pointers must be 16-byte aligned.
+ *           multiples of 8, Q, K and V row strides below 2^24 elements, and
+ *           every row stride at least head_dim (rows may not overlap) unless
+ *           the dense tensor has a single row; base pointers must be 16-byte
+ *           aligned.
  * cu_seqlens_q, cu_seqlens_k  device int32 arrays of B + 1 offsets, both NULL
  *           (dense) or both set (packed).  Their contents are not checked:
  *           the caller guarantees cu[0] = 0, non-decreasing, every length
@@ -141,6 +147,45 @@ MI_ATTN_API mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const voi
                              const int32_t* cu_seqlens_k,
                              float scale, int32_t causal,
                              struct ihipStream_t* stream);
+
+/* Kernels mi_attn_fwd_select can run. */
+typedef enum mi_attn_kernel {
+    MI_ATTN_KERNEL_MFMA = 0,    /* the matrix-core kernel mi_attn_fwd runs   */
+    MI_ATTN_KERNEL_SCALAR = 1   /* scalar fp32 kernel, one lane per query
+                                   row: an independent second implementation
+                                   for cross-checks, far slower              */
+} mi_attn_kernel_t;
+
+/*
+ * mi_attn_fwd_select — mi_attn_fwd with the kernel and, for causal inputs,
+ * the order of the query tiles chosen by the caller.  For tests and
+ * diagnostics: every choice computes the same function as mi_attn_fwd
+ * (bit-identical results are not promised across kernels).
+ *
+ * kernel        MI_ATTN_KERNEL_MFMA or MI_ATTN_KERNEL_SCALAR.
+ * causal_order  MFMA kernel, causal inputs only (ignored otherwise):
+ *               -1 the library's default for the head dimension;
+ *                0 one query tile per work-group, heaviest first;
+ *                1 query tiles t and n-1-t in one work-group;
+ *                2 one query tile per work-group, the first half of the grid
+ *                  heaviest first and the second half lightest first.
+ * Other arguments, validation, ownership and errors as for mi_attn_fwd; an
+ * unknown kernel or order returns MI_ATTN_ERR_ARG with nothing enqueued.
+ */
+MI_ATTN_API mi_attn_status_t mi_attn_fwd_select(const void* q, const void* k, const void* v,
+                             void* o, float* lse,
+                             mi_attn_dtype_t in_dtype, mi_attn_dtype_t out_dtype,
+                             int32_t batch, int32_t hq, int32_t hkv,
+                             int32_t lq, int32_t lk, int32_t head_dim,
+                             const mi_attn_strides_t* q_strides,
+                             const mi_attn_strides_t* k_strides,
+                             const mi_attn_strides_t* v_strides,
+                             const mi_attn_strides_t* o_strides,
+                             const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k,
+                             float scale, int32_t causal,
+                             struct ihipStream_t* stream,
+                             mi_attn_kernel_t kernel, int32_t causal_order);
 
 /* Static, human-readable text for a status code (never NULL). */
 MI_ATTN_API const char* mi_attn_status_string(mi_attn_status_t status);

@@ -202,28 +202,55 @@ def online_softmax_ul(scores, values, boundaries):
     return {"out": u / ell, "lse": m + math.log(ell), "trace": trace}
 
 
-def online_softmax_normalised(scores, values, boundaries):
-    """The normalised form of the same recurrence for ONE query row.
+def _block_partial(s_blk, v_blk):
+    """One key block on its own: (m_b, l_b, o_b) with m_b its max score,
+    l_b = sum exp(s - m_b) and o_b the block's normalised output (its
+    weighted value sum divided by l_b).  None if the block has no visible key.
+    """
+    m_b = float(s_blk.max())
+    if m_b == NEG_INF:
+        return None
+    w = np.exp(s_blk - m_b)
+    l_b = float(w.sum())
+    return m_b, l_b, (w @ v_blk) / l_b
 
-    Keeps m, l and o = (partial output already divided by l); a new block
-    gives alpha = exp(m - m_new), l_new = alpha*l + sum(p) and
-    o_new = (alpha*l*o + p.V) / l_new.  Returns (o, lse).
+
+def _merge_normalised(a, b):
+    """Combine two normalised partial results over disjoint key sets.
+
+    Both are re-expressed relative to the larger max m: their exp-sums are
+    scaled by exp(m_side - m) (the rescaling factor r of section 3.1) and the
+    merged output is the exp-sum-weighted mean of the two outputs.
+    """
+    if a is None:
+        return b
+    if b is None:
+        return a
+    m = max(a[0], b[0])
+    la = a[1] * math.exp(a[0] - m)
+    lb = b[1] * math.exp(b[0] - m)
+    ell = la + lb
+    return m, ell, (la * a[2] + lb * b[2]) / ell
+
+
+def online_softmax_normalised(scores, values, boundaries):
+    """The normalised-output form of the recurrence for ONE query row.
+
+    The state after each block is (m, l, o) with o already divided by l (the
+    Day-14 notes keep o in this form).  Each key block is reduced to its own
+    normalised partial result, which is merged into the running state by the
+    combination rule above: the old state's weight is alpha * l with
+    alpha = exp(m - m_new), the block's is its exp-sum relative to m_new.
+    Returns (o, lse).
     """
     s = np.asarray(scores, dtype=np.float64).reshape(-1)
     val = np.asarray(values, dtype=np.float64).reshape(s.shape[0], -1)
-    m, ell = NEG_INF, 0.0
-    o = np.zeros(val.shape[1], dtype=np.float64)
+    state = None
     for a, b in _blocks(s.shape[0], boundaries):
-        m_new = max(m, float(s[a:b].max()))
-        if m_new == NEG_INF:
-            continue
-        alpha = math.exp(m - m_new)
-        p = np.exp(s[a:b] - m_new)
-        l_new = alpha * ell + float(p.sum())
-        o = (alpha * ell * o + p @ val[a:b]) / l_new
-        m, ell = m_new, l_new
-    if m == NEG_INF:
-        return o, NEG_INF
+        state = _merge_normalised(state, _block_partial(s[a:b], val[a:b]))
+    if state is None:
+        return np.zeros(val.shape[1], dtype=np.float64), NEG_INF
+    m, ell, o = state
     return o, m + math.log(ell)
 
 

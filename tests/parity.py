@@ -63,14 +63,16 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, tol_o=TOL_O, tol_lse=TOL_LSE,
 
 
 def dense_case(b, hq, hkv, lq, lk, d, dtype, causal, scale=None,
-               out_dtype=None, seed=0, layout="bhsd"):
+               out_dtype=None, seed=0, layout="bhsd", **select):
+    """One dense case through the ABI against the oracle; select may hold
+    kernel= / causal_order= for mi_attn_fwd_select."""
     q, k, v = workloads.make_dense(b, hq, hkv, lq, lk, d, dtype, seed)
     if layout == "bshd":
         qg, kg, vg = (t.transpose(1, 2).contiguous() for t in (q, k, v))
     else:
         qg, kg, vg = q, k, v
     o, lse = run_gpu(qg, kg, vg, causal=causal, scale=scale,
-                     out_dtype=out_dtype, layout=layout)
+                     out_dtype=out_dtype, layout=layout, **select)
     if layout == "bshd":
         o = o.transpose(0, 2, 1, 3)
     o_ref, l_ref = oracle.attention(workloads.to_f64(q), workloads.to_f64(k),

@@ -28,8 +28,9 @@ def _header():
 def test_exports_every_declared_function():
     names = re.findall(r"MI_ATTN_API\s+[\w\s\*]+?\b(mi_attn_\w+)\s*\(",
                        _header())
-    assert set(names) == {"mi_attn_fwd", "mi_attn_status_string",
-                          "mi_attn_version", "mi_attn_last_hip_error"}
+    assert set(names) == {"mi_attn_fwd", "mi_attn_fwd_select",
+                          "mi_attn_status_string", "mi_attn_version",
+                          "mi_attn_last_hip_error"}
     for n in names:
         assert hasattr(mi.lib(), n), n
 
@@ -44,7 +45,8 @@ def test_enum_values_match_header():
     for code, name in mi.STATUS_NAMES.items():
         assert re.search(rf"\b{name}\s*=\s*{code}\b", h), name
     for name, code in (("MI_ATTN_F16", 0), ("MI_ATTN_BF16", 1),
-                       ("MI_ATTN_F32", 2)):
+                       ("MI_ATTN_F32", 2), ("MI_ATTN_KERNEL_MFMA", 0),
+                       ("MI_ATTN_KERNEL_SCALAR", 1)):
         assert re.search(rf"\b{name}\s*=\s*{code}\b", h)
 
 
@@ -60,11 +62,13 @@ A = 0x10000          # fake 16-byte-aligned addresses (never dereferenced)
 
 def call(q=A, k=A * 2, v=A * 3, o=A * 4, lse=A * 5, in_dt=0, out_dt=0,
          b=1, hq=2, hkv=1, lq=16, lk=16, d=64, qs=None, ks=None, vs=None,
-         os_=None, cuq=None, cuk=None, scale=0.125, causal=0):
+         os_=None, cuq=None, cuk=None, scale=0.125, causal=0, select=None):
     ref = lambda s: None if s is None else ctypes.byref(s)
-    return mi.lib().mi_attn_fwd(q, k, v, o, lse, in_dt, out_dt, b, hq, hkv,
-                                lq, lk, d, ref(qs), ref(ks), ref(vs),
-                                ref(os_), cuq, cuk, scale, causal, None)
+    args = (q, k, v, o, lse, in_dt, out_dt, b, hq, hkv, lq, lk, d, ref(qs),
+            ref(ks), ref(vs), ref(os_), cuq, cuk, scale, causal, None)
+    if select is None:
+        return mi.lib().mi_attn_fwd(*args)
+    return mi.lib().mi_attn_fwd_select(*args, *select)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -87,6 +91,18 @@ def call(q=A, k=A * 2, v=A * 3, o=A * 4, lse=A * 5, in_dt=0, out_dt=0,
     (dict(qs=Strides(0, 64, 1 << 24)), 3),
     (dict(ks=Strides(0, 64, 1 << 24)), 3),
     (dict(vs=Strides(0, 64, 1 << 25)), 3),
+    # rows may not overlap: row stride 0 (an expanded view) or below head_dim
+    (dict(qs=Strides(0, 0, 0)), 3), (dict(ks=Strides(0, 0, 0)), 3),
+    (dict(vs=Strides(0, 0, 0)), 3), (dict(os_=Strides(0, 0, 0)), 3),
+    (dict(qs=Strides(2048, 1024, 56)), 3), (dict(ks=Strides(2048, 1024, 32)), 3),
+    (dict(vs=Strides(2048, 1024, 8)), 3), (dict(os_=Strides(2048, 1024, 48)), 3),
+    (dict(d=128, ks=Strides(4096, 2048, 64)), 3),
+    (dict(d=128, qs=Strides(4096, 2048, 120)), 3),
+    (dict(cuq=A * 6, cuk=A * 7, qs=Strides(0, 64, 0)), 3),   # packed: always
+    # mi_attn_fwd_select: unknown kernel or causal order
+    (dict(select=(2, -1)), 6), (dict(select=(-1, -1)), 6),
+    (dict(select=(0, 3)), 6), (dict(select=(0, -2)), 6),
+    (dict(select=(1, 0), in_dt=3), 4),
 ])
 def test_rejected_before_any_hip_call(kw, code):
     assert call(**kw) == code

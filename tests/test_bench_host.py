@@ -98,3 +98,22 @@ def test_bench_json_line_on_gpu():
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert rec["cpu_baseline"]["kind"] == "oracle" and rec["cpu_baseline"]["cores"] >= 1
     assert rec["parity"]["pass"]
+
+
+def test_batches_cover_exactly_the_timed_steps():
+    bench = _bench()
+    for steps in (1, 2, 3, 5, 7, 20, 200, 201):
+        sizes = bench.batch_sizes(steps)
+        assert sum(sizes) == steps and 1 <= len(sizes) <= 5
+        assert max(sizes) - min(sizes) <= 1
+
+
+def test_metric_labels():
+    bench = _bench()
+    labels = {n: bench.metric_label(w) for n, w in workloads.WORKLOADS.items()}
+    # the headline keeps the metric string it is quoted on
+    assert labels["causal_b2h16"] == ("attn fwd TFLOP/s + % of fp16 MFMA peak, "
+                                      "B2 H16 N2048 d64 causal")
+    assert len(set(labels.values())) == len(labels)
+    assert "Hq32 Hkv8" in labels["gqa_causal"] and "causal" in labels["gqa_causal"]
+    assert "Lq8192 Lk8192" in labels["long_8k"] and "bf16" in labels["long_8k"]

@@ -24,8 +24,11 @@ F16, BF16 = torch.float16, torch.bfloat16
 # The five named workloads at their full sizes
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["tiny", "causal_b2h16", "bert_varlen"])
+@pytest.mark.parametrize("name", ["tiny", "causal_b2h16", "bert_varlen",
+                                  "gqa_causal", "long_8k"])
 def test_workload_full(name):
+    """Every output element and LSE of the workload against the fp64 oracle
+    (all heads; the two d = 128 workloads take the oracle ~5-15 s)."""
     w = workloads.WORKLOADS[name]
     inp = workloads.make(name, seed=0)
     note(f"workload {name} seed 0 (full oracle)")
@@ -44,26 +47,10 @@ def test_workload_full(name):
         cu_seqlens_k=inp.get("cu_seqlens_k"))
     eo, el = compare(o, lse, o_ref, l_ref)
     note(f"  err_O {eo:.3e}  err_LSE {el:.3e}")
-
-
-@pytest.mark.parametrize("name,heads", [("gqa_causal", [0, 5, 18, 31]),
-                                        ("long_8k", [0, 7, 15])])
-def test_workload_full_size_sampled_heads(name, heads):
-    """Full-size launch; the oracle recomputes a sample of whole heads."""
-    w = workloads.WORKLOADS[name]
-    inp = workloads.make(name, seed=0)
-    note(f"workload {name} seed 0 (oracle on heads {heads})")
-    o, lse = run_gpu(inp["q"], inp["k"], inp["v"], causal=w.causal,
-                     scale=w.scale)
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    g = w.hq // w.hkv
-    f64 = workloads.to_f64
-    q = f64(inp["q"])[:, heads]
-    k = f64(inp["k"])[:, [h // g for h in heads]]
-    v = f64(inp["v"])[:, [h // g for h in heads]]
-    o_ref, l_ref = oracle.attention(q, k, v, scale=w.scale, causal=w.causal)
-    eo, el = compare(o[:, heads], lse[:, heads], o_ref, l_ref)
-    note(f"  err_O {eo:.3e}  err_LSE {el:.3e}")
+    if not w.varlen and w.hq > 1:
+        per_head = np.max(np.abs(o - o_ref), axis=(0, 2, 3))
+        worst = int(np.argmax(per_head))
+        note(f"  worst head {worst}: err_O {per_head[worst]:.3e}")
 
 
 # ---------------------------------------------------------------------------
@@ -154,17 +141,18 @@ def test_cross_attention_lengths(lq, lk, causal):
     dense_case(2, 2, 1, lq, lk, 64, BF16, causal)
 
 
-# Group sizes 1, 2, 3, 4, 7, 16, 33 for the kv-head map.  The extra sizes run
-# in fp16: with P rounded to bf16 and a bf16 output, early causal rows (|O|
-# above 2) reach the 1e-2 bar by rounding alone (15/5 causal, seed 0: the
-# error a CPU emulation of that rounding predicts is 1.0018e-2).
-@pytest.mark.parametrize("hq,hkv,dtype", [(4, 1, BF16), (8, 2, BF16), (6, 3, BF16),
-                                          (4, 4, BF16), (15, 5, F16), (14, 2, F16),
-                                          (32, 2, F16), (33, 1, F16)])
+# Group sizes 1, 2, 3, 4, 7, 16, 33 for the kv-head map, in both input types.
+# bf16 causal is the tight case: early rows see few keys, |O| passes 2 and the
+# bf16 output rounding alone costs up to 7.8e-3 (15/5 causal seed 0: the
+# rounding floor of the exact result is 7.75e-3).
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (8, 2), (6, 3), (4, 4), (15, 5),
+                                    (14, 2), (32, 2), (33, 1)])
+@pytest.mark.parametrize("dtype", [F16, BF16])
 @pytest.mark.parametrize("causal", [False, True])
 def test_gqa(hq, hkv, dtype, causal):
     note(f"gqa {hq}/{hkv} causal {causal} {dtype}")
-    dense_case(2, hq, hkv, 200, 200, 128, dtype, causal)
+    eo, _ = dense_case(2, hq, hkv, 200, 200, 128, dtype, causal)
+    note(f"  err_O {eo:.3e}")
 
 
 def test_gqa_equals_repeated_heads_on_gpu():
@@ -290,19 +278,29 @@ def test_empty_batch_is_noop():
     assert o.shape == q.shape and lse.shape == (0, 2, 16)
 
 
-def test_dominant_key():
-    """One key scores far above the rest: the output is that key's value."""
-    note("dominant key")
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("j_dom", [23, 123, 299])
+def test_dominant_key(dtype, j_dom):
+    """One key scores far above the rest: the output is that key's value.
+
+    In the first key tile the dominant probability is the row's reference
+    (exactly 1), so the output is the value to fp32 rounding.  In a later
+    tile the probability is rounded to the input type for the PV product and
+    the output is normalised by the fp32 sum, so it carries that rounding:
+    at most 2^-11 (fp16) or 2^-9 (bf16) of the value.
+    """
+    note(f"dominant key {j_dom} {dtype}")
     d = 64
-    q = torch.zeros(1, 1, 4, d, dtype=BF16)
+    q = torch.zeros(1, 1, 4, d, dtype=dtype)
     q[..., 0] = 8.0
     gen = torch.Generator().manual_seed(10)
-    k = (0.1 * torch.randn(1, 1, 300, d, generator=gen)).to(BF16)
-    k[0, 0, 123, 0] = 8.0
-    v = torch.randn(1, 1, 300, d, generator=gen).to(BF16)
+    k = (0.1 * torch.randn(1, 1, 300, d, generator=gen)).to(dtype)
+    k[0, 0, j_dom, 0] = 8.0
+    v = torch.randn(1, 1, 300, d, generator=gen).to(dtype)
     o, lse = run_gpu(q, k, v, scale=1.0, out_dtype=torch.float32)
-    want = workloads.to_f64(v)[0, 0, 123]
-    assert np.max(np.abs(o[0, 0] - want[None])) <= 1e-5
+    want = workloads.to_f64(v)[0, 0, j_dom]
+    rel = 1e-6 if j_dom < 64 else (2.0 ** -11 if dtype == F16 else 2.0 ** -9)
+    assert np.all(np.abs(o[0, 0] - want[None]) <= rel * np.abs(want)[None] + 1e-6)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -336,6 +334,29 @@ def test_reference_jump(d, causal, dtype, boost):
     note(f"  err_O {eo:.3e}  err_LSE {el:.3e}")
 
 
+def test_overflow_with_large_values():
+    """bf16: a late key scores ~72-180 log2 units above the first tile's
+    maximum and its value is large, so in the short form the probability
+    approaches the fp32 range and P * V overflows; the q-tile must be redone
+    in the safe form.  Compared with a relative bound (the values are far
+    from N(0, 1))."""
+    note("overflow with large values (bf16)")
+    b, h, lq, lk, j_big, d = 1, 2, 300, 300, 200, 128
+    q, k, v = workloads.make_dense(b, h, h, lq, lk, d, BF16, seed=22)
+    q, k, v = q.float(), k.float(), v.float()
+    q[..., 0] = q[..., 0].abs() + 2.0
+    k[:, :, j_big, 0] = 25.0 * math.sqrt(d)     # 25 q0 log-e units, q0 in [2, 5]
+    v[:, :, j_big] = 3.0e4
+    q, k, v = q.to(BF16), k.to(BF16), v.to(BF16)
+    for causal in (False, True):
+        o, lse = run_gpu(q, k, v, causal=causal, out_dtype=torch.float32)
+        o_ref, l_ref = oracle.attention(workloads.to_f64(q), workloads.to_f64(k),
+                                        workloads.to_f64(v), causal=causal)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        assert np.all(np.abs(o - o_ref) <= 1e-2 * np.maximum(1.0, np.abs(o_ref)))
+        assert np.max(np.abs(lse - l_ref)) <= TOL_LSE
+
+
 def test_long_row_with_large_fp16_sums():
     """fp16, 300000 keys with near-uniform scores: every lane's fp32 row sum
     passes 65504 while no probability leaves the fp16 range."""
@@ -347,28 +368,30 @@ def test_long_row_with_large_fp16_sums():
     compare(o, lse, o_ref, l_ref)
 
 
-# The scalar reference kernel (MI_ATTN_KERNEL=simple): a second, independent
-# HIP implementation, checked against the oracle on its own.
+# The scalar reference kernel (mi_attn_fwd_select with MI_ATTN_KERNEL_SCALAR):
+# a second, independent HIP implementation, checked against the oracle.
+SCALAR = 1
+
+
 @pytest.mark.parametrize("b,hq,hkv,lq,lk,d,dtype,causal", [
     (1, 2, 2, 130, 250, 64, BF16, False),
     (2, 4, 2, 200, 200, 64, F16, True),
     (1, 6, 3, 129, 300, 128, BF16, True),
     (1, 2, 1, 300, 129, 128, F16, True),     # fewer keys: early rows see none
 ])
-def test_scalar_kernel(monkeypatch, b, hq, hkv, lq, lk, d, dtype, causal):
-    monkeypatch.setenv("MI_ATTN_KERNEL", "simple")
+def test_scalar_kernel(b, hq, hkv, lq, lk, d, dtype, causal):
     note(f"scalar kernel b{b} hq{hq} hkv{hkv} lq{lq} lk{lk} d{d} {dtype} causal {causal}")
-    dense_case(b, hq, hkv, lq, lk, d, dtype, causal)
+    dense_case(b, hq, hkv, lq, lk, d, dtype, causal, kernel=SCALAR)
 
 
-def test_scalar_kernel_varlen(monkeypatch):
-    monkeypatch.setenv("MI_ATTN_KERNEL", "simple")
+def test_scalar_kernel_varlen():
     lens_q = [5, 130, 0, 77]
     lens_k = [9, 130, 4, 0]
     note(f"scalar kernel varlen lens_q {lens_q} lens_k {lens_k}")
     q, k, v, cq, ck = workloads.make_packed(lens_q, lens_k, 4, 2, 64, BF16, seed=3)
     o, lse = run_gpu(q, k, v, cu_seqlens_q=cq, cu_seqlens_k=ck,
-                     max_seqlen_q=max(lens_q), max_seqlen_k=max(lens_k), causal=True)
+                     max_seqlen_q=max(lens_q), max_seqlen_k=max(lens_k), causal=True,
+                     kernel=SCALAR)
     f64 = workloads.to_f64
     o_ref, l_ref = oracle.attention(f64(q), f64(k), f64(v), causal=True,
                                     cu_seqlens_q=cq.numpy(), cu_seqlens_k=ck.numpy())
@@ -398,11 +421,11 @@ def test_repeat_runs_are_bit_identical():
 # Causal shapes around the q-tile pairing: head counts that are not multiples
 # of 8, Lq != Lk both ways (bottom-right alignment, rows with no key), an odd
 # q-tile count, and every causal q-tile order the kernel has
-# (MI_ATTN_CAUSAL_PAIRS: 0 heaviest first, 1 q-tiles t and n-1-t in one
-# work-group, 2 grid halves heaviest-first and lightest-first).
+# (mi_attn_fwd_select's causal_order: 0 heaviest first, 1 q-tiles t and
+# n-1-t in one work-group, 2 grid halves heaviest-first and lightest-first).
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("order", ["0", "1", "2"])
+@pytest.mark.parametrize("order", [0, 1, 2])
 @pytest.mark.parametrize("b,h,lq,lk,d,dtype", [
     (1, 3, 1024, 1024, 64, F16),
     (2, 5, 1024, 1024, 64, BF16),
@@ -412,7 +435,6 @@ def test_repeat_runs_are_bit_identical():
     (1, 2, 1152, 1152, 64, F16),     # odd q-tile count: the middle one alone
     (1, 2, 2048, 2048, 128, F16),
 ])
-def test_causal_tile_orders(monkeypatch, order, b, h, lq, lk, d, dtype):
-    monkeypatch.setenv("MI_ATTN_CAUSAL_PAIRS", order)
+def test_causal_tile_orders(order, b, h, lq, lk, d, dtype):
     note(f"causal order {order} b{b} h{h} lq{lq} lk{lk} d{d} {dtype}")
-    dense_case(b, h, h, lq, lk, d, dtype, True)
+    dense_case(b, h, h, lq, lk, d, dtype, True, causal_order=order)
