@@ -132,13 +132,13 @@ mi_attn_status_t forward(const void* q, const void* k, const void* v,
     p.causal_pairs = causal_order;
 
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const hipError_t err =
-        kernel == MI_ATTN_KERNEL_SCALAR
-            ? mi_attn::launch_simple(p, (int)in_dtype, (int)out_dtype,
-                                     head_dim, st)
-            : head_dim == 64
-                  ? mi_attn::launch_mfma_d64(p, (int)in_dtype, (int)out_dtype, st)
-                  : mi_attn::launch_mfma_d128(p, (int)in_dtype, (int)out_dtype, st);
+    hipError_t err;
+    if (kernel == MI_ATTN_KERNEL_SCALAR)
+        err = mi_attn::launch_simple(p, (int)in_dtype, (int)out_dtype, head_dim, st);
+    else if (head_dim == 64)
+        err = mi_attn::launch_mfma_d64(p, (int)in_dtype, (int)out_dtype, st);
+    else
+        err = mi_attn::launch_mfma_d128(p, (int)in_dtype, (int)out_dtype, st);
     if (err != hipSuccess) {
         g_last_hip_error = (int32_t)err;
         return MI_ATTN_ERR_HIP;
