@@ -43,6 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}   # MI355X dense MFMA, per GPU
+PEAK_HBM_GBS = 8000.0                            # MI355X HBM3E, per GPU
 # what the hot kernel is built from: its template, instantiations and flags
 KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_61_amd", *parts) for parts in
                (("csrc", "attn_fwd_mfma.hpp"), ("csrc", "attn_fwd_mfma_d64.hip"),
@@ -109,6 +110,9 @@ def metric_label(w):
     import workloads
     if w.name == workloads.HEADLINE:
         return HEADLINE_METRIC
+    if w.decode:
+        return (f"attn decode GB/s (HBM roofline), B{w.batch} Hq{w.hq} Hkv{w.hkv} "
+                f"Lq{w.lq} Lk{w.lk} d{w.d} {w.in_dtype}")
     shape = (f"varlen B{w.batch} H{w.hq} max L{w.lq}" if w.varlen else
              f"B{w.batch} Hq{w.hq} Hkv{w.hkv} Lq{w.lq} Lk{w.lk}")
     return (f"attn fwd TFLOP/s + % of {w.in_dtype} MFMA peak, {shape} d{w.d}"
@@ -204,7 +208,7 @@ def summarize_counters(dirpath, name, write_record):
     inp = workloads.make(name, seed=0)
     flops = 4.0 * w.d * w.hq * visible_pairs(w, inp.get("lengths"))
     nbytes = algorithmic_bytes(w, inp)
-    kern = "attn_fwd_mfma_kernel"
+    kern = "attn_decode_kernel" if w.decode else "attn_fwd_mfma_kernel"
     wl = f"--workload {name} "
     cmds = {
         "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o t -- python3 bench.py {wl}--steps 50 --warmup 5 --no-cpu-baseline",
@@ -247,6 +251,8 @@ def summarize_counters(dirpath, name, write_record):
         f"{statistics.median(dur) / 1e3:.2f} us, min {min(dur) / 1e3:.2f} us |",
         f"| algorithmic TFLOP/s at the mean duration | {flops / t_avg / 1e12:.1f} "
         f"({100 * flops / t_avg / 1e12 / PEAK_TFLOPS[w.in_dtype]:.2f} % of {PEAK_TFLOPS[w.in_dtype]}) |",
+        f"| algorithmic GB/s at the mean duration | {nbytes / t_avg / 1e9:.0f} "
+        f"({100 * nbytes / t_avg / 1e9 / PEAK_HBM_GBS:.1f} % of {PEAK_HBM_GBS:.0f}) |",
         f"| read requests 32 B / 64 B / 128 B (all) | {n32:.0f} / {n64:.0f} / {n128:.0f} ({nall:.0f}) |",
         f"| HBM read bytes (32·n32 + 64·n64 + 128·n128) | {read_b / 2**20:.2f} MiB = "
         f"{read_b / in_b:.3f} x Q+K+V ({in_b / 2**20:.2f} MiB) |",
@@ -346,8 +352,17 @@ def main():
         lse = torch.empty((w.batch, w.hq, w.lq), dtype=torch.float32,
                           device=dev)
 
-    def step():
-        mi.mi_attn_fwd(q, k, v, o, lse, **kw)
+    workspace = None
+    if w.decode:
+        nws = mi.mi_attn_decode_workspace_size(w.batch, w.hq, w.hkv, w.lq, w.lk, w.d)
+        if nws:
+            workspace = torch.zeros(nws, dtype=torch.uint8, device=dev)
+
+        def step():
+            mi.mi_attn_decode(q, k, v, o, lse, workspace=workspace, **kw)
+    else:
+        def step():
+            mi.mi_attn_fwd(q, k, v, o, lse, **kw)
 
     lengths = inp.get("lengths")
     flops = 4.0 * w.d * w.hq * visible_pairs(w, lengths)
@@ -405,6 +420,7 @@ def main():
     ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
 
     tflops = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
     peak_tf = PEAK_TFLOPS[w.in_dtype]
     props = torch.cuda.get_device_properties(dev)
     counters = load_counter_record(name)
@@ -415,10 +431,24 @@ def main():
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(w, inp, o_gpu, lse_gpu, flops)
 
+    if w.decode:
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "traffic": None if counters is None else counters.get("hbm_bytes_per_launch"),
+                    "mfma_busy": None if counters is None else counters.get("mfma_busy"),
+                    "algorithmic_bytes": nbytes, "kernel": "attn_decode_kernel"}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 3),
+                    "peak": peak_tf, "unit": "TFLOP/s",
+                    "frac": round(tflops / peak_tf, 4),
+                    "traffic": None if counters is None else counters.get("hbm_bytes_per_launch"),
+                    "mfma_busy": None if counters is None else counters.get("mfma_busy"),
+                    "algorithmic_bytes": nbytes,
+                    "kernel": "attn_fwd_mfma_kernel"}
     rec = {
         "metric": metric_label(w),
-        "value": round(tflops, 3),
-        "unit": "TFLOP/s",
+        "value": round(gbs, 1) if w.decode else round(tflops, 3),
+        "unit": "GB/s" if w.decode else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -433,23 +463,19 @@ def main():
                    "causal": w.causal, "varlen": w.varlen,
                    "in_dtype": w.in_dtype, "out_dtype": w.out_dtype,
                    "lengths": lengths},
-        "pct_of_peak": round(100.0 * tflops / peak_tf, 2),
+        "pct_of_peak": round(100.0 * (gbs / PEAK_HBM_GBS if w.decode else tflops / peak_tf), 2),
         "algorithmic_flops": flops,
+        "tflops": round(tflops, 3),
         # the common convention: 4*B*H*Lq*Lk*d, halved for causal
         "flops_common_convention": (2.0 if w.causal else 4.0) * w.batch *
         w.hq * w.lq * w.lk * w.d,
         "ms_per_step_median_batch": round(ms_median, 6),
         "batches": sizes,
         "ms_per_step_eager": round(ms_eager, 6),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
-                     "peak": peak_tf, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak_tf, 4),
-                     "traffic": None if counters is None else counters.get("hbm_bytes_per_launch"),
-                     "mfma_busy": None if counters is None else counters.get("mfma_busy"),
-                     "algorithmic_bytes": nbytes,
-                     "kernel": "attn_fwd_mfma_kernel"},
+        "roofline": roofline,
         "memory": {"peak_allocated_bytes": int(peak),
                    "inputs_outputs_bytes": int(resident),
+                   "workspace_bytes": 0 if workspace is None else workspace.numel(),
                    "ratio": round(peak / resident, 4) if resident else None},
         "cpu_baseline": base,
         "parity": parity,

@@ -9,9 +9,13 @@ Entry points mirror the C ABI of include/mi_attn.h:
 * mi_attn_fwd(q, k, v, o, lse, ...)  -- writes into caller-provided tensors;
 * mi_attn_fwd_select(..., kernel=, causal_order=) -- the same with the kernel
   and the causal tile order chosen explicitly (tests and diagnostics);
+* mi_attn_decode(q, k, v, o, lse, ...) -- a few query rows against a long
+  key/value cache, keys split across work-groups (needs a workspace);
+* mi_attn_decode_workspace_size(...), mi_attn_decode_splits(...);
 * mi_attn_status_string(code), mi_attn_version(), mi_attn_last_hip_error();
 
-plus forward(q, k, v, ...) -> (out, lse), which allocates the outputs.
+plus forward(q, k, v, ...) -> (out, lse) and decode(q, k, v, ...) ->
+(out, lse), which allocate the outputs (and decode's workspace).
 """
 
 import ctypes
@@ -31,7 +35,7 @@ _DTYPE_CODE = {torch.float16: MI_ATTN_F16, torch.bfloat16: MI_ATTN_BF16,
 STATUS_NAMES = {0: "MI_ATTN_OK", 1: "MI_ATTN_ERR_NULL", 2: "MI_ATTN_ERR_SHAPE",
                 3: "MI_ATTN_ERR_LAYOUT", 4: "MI_ATTN_ERR_DTYPE",
                 5: "MI_ATTN_ERR_UNSUPPORTED", 6: "MI_ATTN_ERR_ARG",
-                7: "MI_ATTN_ERR_HIP"}
+                7: "MI_ATTN_ERR_HIP", 8: "MI_ATTN_ERR_WORKSPACE"}
 
 
 class Strides(ctypes.Structure):
@@ -65,6 +69,14 @@ def _load():
                                 ctypes.c_float, i32, P]
     lib.mi_attn_fwd_select.restype = ctypes.c_int
     lib.mi_attn_fwd_select.argtypes = lib.mi_attn_fwd.argtypes + [ctypes.c_int, i32]
+    lib.mi_attn_decode.restype = ctypes.c_int
+    lib.mi_attn_decode.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int,
+                                   i32, i32, i32, i32, i32, i32, S, S, S, S, P,
+                                   ctypes.c_float, i32, i32, P, ctypes.c_size_t, P]
+    lib.mi_attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.mi_attn_decode_workspace_size.argtypes = [i32] * 7
+    lib.mi_attn_decode_splits.restype = i32
+    lib.mi_attn_decode_splits.argtypes = [i32] * 7
     lib.mi_attn_status_string.restype = ctypes.c_char_p
     lib.mi_attn_status_string.argtypes = [ctypes.c_int]
     lib.mi_attn_version.restype = i32
@@ -194,6 +206,78 @@ def _call(q, k, v, o, lse, causal, scale, cu_seqlens_q, cu_seqlens_k,
         if st == 7:
             detail = f"hipError {mi_attn_last_hip_error()}"
         raise MiAttnError(st, detail)
+
+
+def mi_attn_decode_workspace_size(batch, hq, hkv, lq, lk, head_dim, num_splits=0):
+    """Bytes of workspace mi_attn_decode needs (0: a single split)."""
+    return int(_lib.mi_attn_decode_workspace_size(batch, hq, hkv, lq, lk, head_dim,
+                                                  num_splits))
+
+
+def mi_attn_decode_splits(batch, hq, hkv, lq, lk, head_dim, num_splits=0):
+    """The key splits mi_attn_decode uses for these sizes."""
+    return int(_lib.mi_attn_decode_splits(batch, hq, hkv, lq, lk, head_dim, num_splits))
+
+
+def mi_attn_decode(q, k, v, o, lse=None, *, seqlens_k=None, causal=True, scale=None,
+                   num_splits=0, workspace=None, stream=None):
+    """Call mi_attn_decode on caller-provided tensors (one device).
+
+    q, o: [B, Hq, Lq, d] (Lq <= 32); k, v: the cache [B, Hkv, Lk, d]; lse
+    [B, Hq, Lq] float32 or None; seqlens_k: int32 [B] keys per sequence or
+    None (all Lk).  workspace: a uint8 tensor of at least
+    mi_attn_decode_workspace_size(...) bytes whose counters start at zero
+    (torch.zeros), or None when that size is 0.
+    """
+    for t in (q, k, v, o, lse, seqlens_k, workspace):
+        if t is not None and (not t.is_cuda or t.device != q.device):
+            raise MiAttnError(6, "every tensor must be on q's GPU device")
+    if q.dtype not in _DTYPE_CODE or o.dtype not in _DTYPE_CODE:
+        raise MiAttnError(4, f"{q.dtype} -> {o.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise MiAttnError(4, "q, k and v must share one dtype")
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32
+                                  or not seqlens_k.is_contiguous()):
+        raise MiAttnError(3, "seqlens_k must be contiguous int32")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise MiAttnError(3, "lse must be contiguous float32")
+    d = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    bsz, hq, hkv, lq, lk = _dims(q, k, "bhsd", False)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    qs, ks, vs, os_ = (_strides(t, "bhsd", False) for t in (q, k, v, o))
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size())
+    st = _lib.mi_attn_decode(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+        _DTYPE_CODE[q.dtype], _DTYPE_CODE[o.dtype], bsz, hq, hkv, lq, lk, d,
+        ctypes.byref(qs), ctypes.byref(ks), ctypes.byref(vs), ctypes.byref(os_),
+        _ptr(seqlens_k), float(scale), int(bool(causal)), int(num_splits),
+        ws_ptr, ws_bytes, ctypes.c_void_p(stream))
+    if st != 0:
+        detail = f"hipError {mi_attn_last_hip_error()}" if st == 7 else ""
+        raise MiAttnError(st, detail)
+
+
+def decode(q, k, v, *, seqlens_k=None, causal=True, scale=None, num_splits=0,
+           out_dtype=None, workspace=None, return_lse=True):
+    """Allocate out (and lse, and a zeroed workspace unless given) and run
+    mi_attn_decode; returns (out, lse)."""
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    bsz, hq, hkv, lq, lk = _dims(q, k, "bhsd", False)
+    lse = (torch.empty((bsz, hq, lq), dtype=torch.float32, device=q.device)
+           if return_lse else None)
+    if workspace is None:
+        n = mi_attn_decode_workspace_size(bsz, hq, hkv, lq, lk, q.shape[-1], num_splits)
+        if n > 0:
+            workspace = torch.zeros(n, dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        mi_attn_decode(q, k, v, out, lse, seqlens_k=seqlens_k, causal=causal, scale=scale,
+                       num_splits=num_splits, workspace=workspace)
+    return out, lse
 
 
 def _check_cu(cu, max_len, rows):

@@ -31,6 +31,34 @@ struct FwdParams {
     int32_t causal_pairs;            // causal q-tile order (0, 1, 2; -1 default)
 };
 
+// Parameters of the decode kernel (attn_decode.hip): a few query rows per
+// sequence against a long key/value cache, split along the keys.  Offsets
+// are in elements; tensors are dense [B, H, L, d] views through strides.
+struct DecParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;                      // may be null
+    const int32_t* seqlens_k;        // per-sequence key counts (<= lk), or null
+    int64_t q_sb, q_sh, q_sr;
+    int64_t k_sb, k_sh, k_sr;
+    int64_t v_sb, v_sh, v_sr;
+    int64_t o_sb, o_sh, o_sr;
+    int32_t batch, hq, hkv, lq, lk;
+    int32_t group;                   // hq / hkv query heads per kv head
+    int32_t hpg;                     // query heads per work-group (hpg * lq <= 32)
+    int32_t nqg;                     // query groups per kv head, ceil(group / hpg)
+    int32_t splits;                  // key splits per query group
+    int32_t chunk;                   // keys per split, a multiple of 128
+    float scale_log2;                // |scale| * log2(e)
+    int32_t negate_q;                // 1 when scale < 0
+    int32_t causal;                  // bottom-right: j <= i + Lk_b - Lq
+    float* part_o;                   // [B, Hq, Lq, splits, d] partial outputs
+    float* part_ml;                  // [B, Hq, Lq, splits, 2] (m in log2, l)
+    int32_t* counters;               // [B, hkv, nqg] arrivals, zero between calls
+};
+
 // Storage tags for the element types (16-bit values are kept as raw bits).
 struct f16_t { uint16_t bits; };
 struct bf16_t { uint16_t bits; };
@@ -81,5 +109,7 @@ hipError_t launch_mfma_d64(const FwdParams& p, int in_dtype, int out_dtype,
                           hipStream_t stream);
 hipError_t launch_mfma_d128(const FwdParams& p, int in_dtype, int out_dtype,
                            hipStream_t stream);
+hipError_t launch_decode(const DecParams& p, int in_dtype, int out_dtype, int head_dim,
+                         hipStream_t stream);
 
 }  // namespace mi_attn

@@ -5,7 +5,9 @@
 // checks of the pages' fused-dense binding (dtype, contiguity and shape
 // checks before any launch, an error code instead of a crash) and the
 // training tutorial's constraints (Hkv divides Hq, head_dim a multiple of 8).
+#include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
 
 #include "../../include/mi_attn.h"
@@ -146,9 +148,163 @@ mi_attn_status_t forward(const void* q, const void* k, const void* v,
     return MI_ATTN_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Decode: work split and workspace layout
+// ---------------------------------------------------------------------------
+
+constexpr int kDecMaxRows = 32;          // query rows per decode work-group
+constexpr int kDecMaxLq = 32;
+constexpr int kDecChunkAlign = 128;      // keys: 4 waves x 32-key tiles
+constexpr int kCUs = 256;                // MI355X compute units
+
+struct DecodePlan {
+    int32_t hpg, nqg, splits, chunk;
+    size_t off_ml, off_cnt, bytes;       // workspace layout (bytes == 0: none)
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The split count: the caller's, or enough splits for about one work-group
+// per CU, each with at least 256 keys.
+DecodePlan decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t lq, int32_t lk,
+                       int32_t head_dim, int32_t num_splits) {
+    DecodePlan pl{};
+    const int32_t group = hq / hkv;
+    pl.hpg = std::max(1, std::min(group, kDecMaxRows / std::max(1, lq)));
+    pl.nqg = (group + pl.hpg - 1) / pl.hpg;
+    const int64_t groups = (int64_t)batch * hkv * pl.nqg;
+    const int32_t max_splits = std::max(1, (lk + 255) / 256);
+    int32_t s = num_splits;
+    if (s <= 0) {
+        s = (int32_t)std::max<int64_t>(1, (kCUs + groups - 1) / std::max<int64_t>(1, groups));
+        s = std::min(s, max_splits);
+    }
+    s = std::min(s, std::max(1, (lk + kDecChunkAlign - 1) / kDecChunkAlign));
+    pl.splits = std::max(1, s);
+    const int32_t per = (lk + pl.splits - 1) / pl.splits;
+    pl.chunk = std::max(kDecChunkAlign,
+                        (per + kDecChunkAlign - 1) / kDecChunkAlign * kDecChunkAlign);
+    // splits whose keys all lie past lk would do nothing: drop them
+    pl.splits = std::max(1, std::min(pl.splits, (lk + pl.chunk - 1) / pl.chunk));
+    if (pl.splits == 1) return pl;
+    const size_t rows = (size_t)batch * hq * lq * pl.splits;
+    pl.off_ml = align256(rows * head_dim * 4);
+    pl.off_cnt = pl.off_ml + align256(rows * 2 * 4);
+    pl.bytes = pl.off_cnt + align256((size_t)groups * 4);
+    return pl;
+}
+
+// Validation and launch of the decode path.  `workspace` (bytes) holds the
+// partial results and the arrival counters; the counters must be zero
+// before the first call and are zero again after every call.
+mi_attn_status_t decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                        mi_attn_dtype_t in_dtype, mi_attn_dtype_t out_dtype, int32_t batch,
+                        int32_t hq, int32_t hkv, int32_t lq, int32_t lk, int32_t head_dim,
+                        const mi_attn_strides_t* q_strides, const mi_attn_strides_t* k_strides,
+                        const mi_attn_strides_t* v_strides, const mi_attn_strides_t* o_strides,
+                        const int32_t* seqlens_k, float scale, int32_t causal,
+                        int32_t num_splits, void* workspace, size_t workspace_bytes,
+                        struct ihipStream_t* stream) {
+    if (in_dtype != MI_ATTN_F16 && in_dtype != MI_ATTN_BF16) return MI_ATTN_ERR_DTYPE;
+    if (out_dtype != in_dtype && out_dtype != MI_ATTN_F32) return MI_ATTN_ERR_DTYPE;
+    if (batch < 0 || lq < 0 || lk < 0 || hq < 1 || hkv < 1 || hq % hkv != 0)
+        return MI_ATTN_ERR_SHAPE;
+    if (lq > kDecMaxLq || hq > 65535 || batch > 65535) return MI_ATTN_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return MI_ATTN_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale)) return MI_ATTN_ERR_ARG;
+    if (causal != 0 && causal != 1) return MI_ATTN_ERR_ARG;
+    if (num_splits < 0 || num_splits > 65535) return MI_ATTN_ERR_ARG;
+    if (batch == 0 || lq == 0) return MI_ATTN_OK;
+    const bool no_keys = lk == 0;
+    if (q == nullptr || o == nullptr || (!no_keys && (k == nullptr || v == nullptr)))
+        return MI_ATTN_ERR_NULL;
+    const mi_attn_strides_t qs = q_strides ? *q_strides : default_strides(false, hq, lq, head_dim);
+    const mi_attn_strides_t ks = k_strides ? *k_strides : default_strides(false, hkv, lk, head_dim);
+    const mi_attn_strides_t vs = v_strides ? *v_strides : default_strides(false, hkv, lk, head_dim);
+    const mi_attn_strides_t os = o_strides ? *o_strides : default_strides(false, hq, lq, head_dim);
+    if (!stride_ok(qs) || !stride_ok(ks) || !stride_ok(vs) || !stride_ok(os))
+        return MI_ATTN_ERR_LAYOUT;
+    if (ks.row >= kMaxRowStride || vs.row >= kMaxRowStride) return MI_ATTN_ERR_LAYOUT;
+    if ((lq > 1 && (qs.row < head_dim || os.row < head_dim)) ||
+        (lk > 1 && (ks.row < head_dim || vs.row < head_dim)))
+        return MI_ATTN_ERR_LAYOUT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
+        return MI_ATTN_ERR_LAYOUT;
+    const DecodePlan pl = decode_plan(batch, hq, hkv, lq, lk, head_dim, num_splits);
+    if ((int64_t)hkv * pl.nqg > 65535) return MI_ATTN_ERR_SHAPE;
+    if (pl.bytes > 0) {
+        if (workspace == nullptr) return MI_ATTN_ERR_NULL;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MI_ATTN_ERR_LAYOUT;
+        if (workspace_bytes < pl.bytes) return MI_ATTN_ERR_WORKSPACE;
+    }
+
+    mi_attn::DecParams p{};
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+    p.seqlens_k = seqlens_k;
+    p.q_sb = qs.batch; p.q_sh = qs.head; p.q_sr = qs.row;
+    p.k_sb = ks.batch; p.k_sh = ks.head; p.k_sr = ks.row;
+    p.v_sb = vs.batch; p.v_sh = vs.head; p.v_sr = vs.row;
+    p.o_sb = os.batch; p.o_sh = os.head; p.o_sr = os.row;
+    p.batch = batch; p.hq = hq; p.hkv = hkv; p.lq = lq; p.lk = lk;
+    p.group = hq / hkv;
+    p.hpg = pl.hpg;
+    p.nqg = pl.nqg;
+    p.splits = pl.splits;
+    p.chunk = pl.chunk;
+    p.scale_log2 = (float)std::fmax(std::fabs((double)scale) * 1.4426950408889634074, 1e-30);
+    p.negate_q = scale < 0.0f ? 1 : 0;
+    p.causal = causal;
+    if (pl.bytes > 0) {
+        char* ws = static_cast<char*>(workspace);
+        p.part_o = reinterpret_cast<float*>(ws);
+        p.part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
+        p.counters = reinterpret_cast<int32_t*>(ws + pl.off_cnt);
+    }
+    const hipError_t err = mi_attn::launch_decode(p, (int)in_dtype, (int)out_dtype, head_dim,
+                                                  reinterpret_cast<hipStream_t>(stream));
+    if (err != hipSuccess) {
+        g_last_hip_error = (int32_t)err;
+        return MI_ATTN_ERR_HIP;
+    }
+    return MI_ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t mi_attn_decode_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t lq,
+                                     int32_t lk, int32_t head_dim, int32_t num_splits) {
+    if (batch <= 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || lq <= 0 || lq > kDecMaxLq ||
+        lk < 0 || (head_dim != 64 && head_dim != 128) || num_splits < 0)
+        return 0;
+    return decode_plan(batch, hq, hkv, lq, lk, head_dim, num_splits).bytes;
+}
+
+int32_t mi_attn_decode_splits(int32_t batch, int32_t hq, int32_t hkv, int32_t lq, int32_t lk,
+                              int32_t head_dim, int32_t num_splits) {
+    if (batch <= 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || lq <= 0 || lq > kDecMaxLq ||
+        lk < 0 || (head_dim != 64 && head_dim != 128) || num_splits < 0)
+        return 0;
+    return decode_plan(batch, hq, hkv, lq, lk, head_dim, num_splits).splits;
+}
+
+mi_attn_status_t mi_attn_decode(const void* q, const void* k, const void* v, void* o,
+                                float* lse, mi_attn_dtype_t in_dtype,
+                                mi_attn_dtype_t out_dtype, int32_t batch, int32_t hq,
+                                int32_t hkv, int32_t lq, int32_t lk, int32_t head_dim,
+                                const mi_attn_strides_t* q_strides,
+                                const mi_attn_strides_t* k_strides,
+                                const mi_attn_strides_t* v_strides,
+                                const mi_attn_strides_t* o_strides,
+                                const int32_t* seqlens_k, float scale, int32_t causal,
+                                int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                struct ihipStream_t* stream) {
+    return decode(q, k, v, o, lse, in_dtype, out_dtype, batch, hq, hkv, lq, lk, head_dim,
+                  q_strides, k_strides, v_strides, o_strides, seqlens_k, scale, causal,
+                  num_splits, workspace, workspace_bytes, stream);
+}
 
 mi_attn_status_t mi_attn_fwd(const void* q, const void* k, const void* v,
                              void* o, float* lse, mi_attn_dtype_t in_dtype,
@@ -206,6 +362,9 @@ const char* mi_attn_status_string(mi_attn_status_t status) {
             return "MI_ATTN_ERR_ARG: scale not finite, causal not 0/1, only "
                    "one cu_seqlens pointer given, or an unknown kernel / order";
         case MI_ATTN_ERR_HIP: return "MI_ATTN_ERR_HIP: kernel launch failed";
+        case MI_ATTN_ERR_WORKSPACE:
+            return "MI_ATTN_ERR_WORKSPACE: workspace smaller than "
+                   "mi_attn_decode_workspace_size()";
     }
     return "unknown mi_attn status";
 }

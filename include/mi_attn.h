@@ -36,6 +36,7 @@
 #ifndef MI_ATTN_H
 #define MI_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -70,8 +71,10 @@ typedef enum mi_attn_status {
                                     one of the cu_seqlens pointers given, or
                                     (mi_attn_fwd_select) an unknown kernel or
                                     causal order                              */
-    MI_ATTN_ERR_HIP = 7          /* the kernel launch failed (the HIP error
+    MI_ATTN_ERR_HIP = 7,         /* the kernel launch failed (the HIP error
                                     is kept per thread, see below)            */
+    MI_ATTN_ERR_WORKSPACE = 8    /* mi_attn_decode: workspace smaller than
+                                    mi_attn_decode_workspace_size()           */
 } mi_attn_status_t;
 
 /* Element types. */
@@ -186,6 +189,62 @@ MI_ATTN_API mi_attn_status_t mi_attn_fwd_select(const void* q, const void* k, co
                              float scale, int32_t causal,
                              struct ihipStream_t* stream,
                              mi_attn_kernel_t kernel, int32_t causal_order);
+
+/*
+ * mi_attn_decode — the same operation for a few new query rows per sequence
+ * against a long key/value cache, with the keys split across work-groups
+ * and the partial results merged by log-sum-exp.
+ *
+ * The new queries follow the cached keys (the training-integration
+ * tutorial, section 4.3: with a KV cache the new tokens' positions start at
+ * the cache length), so with causal = 1 query row i of Lq sees keys
+ * j <= i + Lk_b - Lq (bottom-right, as for mi_attn_fwd); causal = 0 sees all
+ * Lk_b keys.  A split's partial (m, l, output) over its keys combines with
+ * the others by the rule of the fusion notes, section 3.1: m = max over the
+ * parts, each part's exp-sum and output scaled by exp(m_part - m).
+ *
+ * q, o      dense [B, Hq, Lq, d] views (strides as for mi_attn_fwd), Lq <= 32.
+ * k, v      the cache, dense [B, Hkv, Lk, d] views.
+ * lse       [B, Hq, Lq] contiguous fp32, or NULL.
+ * seqlens_k device int32 [B]: keys of sequence b are rows 0 .. seqlens_k[b]-1
+ *           of its cache (each <= lk, not checked); NULL means lk for all.
+ * num_splits  key splits per (sequence, kv head): 0 lets the library choose
+ *           (about one work-group per CU, at least 256 keys per split);
+ *           otherwise at most 65535, and capped so every split has keys.
+ * workspace, workspace_bytes  device memory of at least
+ *           mi_attn_decode_workspace_size(...) bytes, 256-byte aligned, or
+ *           NULL when that size is 0 (a single split).  It holds the partial
+ *           results and one arrival counter per query group; the counters
+ *           must be zero before the first call (e.g. a zero-filled buffer)
+ *           and every call leaves them at zero.  Calls that share one
+ *           workspace must not overlap in time.
+ * Other arguments, ownership, validation and errors as for mi_attn_fwd;
+ * Lq above 32 returns MI_ATTN_ERR_SHAPE, a NULL or short workspace
+ * MI_ATTN_ERR_NULL / MI_ATTN_ERR_WORKSPACE, a workspace not 256-byte
+ * aligned MI_ATTN_ERR_LAYOUT.
+ */
+MI_ATTN_API mi_attn_status_t mi_attn_decode(const void* q, const void* k, const void* v,
+                             void* o, float* lse,
+                             mi_attn_dtype_t in_dtype, mi_attn_dtype_t out_dtype,
+                             int32_t batch, int32_t hq, int32_t hkv,
+                             int32_t lq, int32_t lk, int32_t head_dim,
+                             const mi_attn_strides_t* q_strides,
+                             const mi_attn_strides_t* k_strides,
+                             const mi_attn_strides_t* v_strides,
+                             const mi_attn_strides_t* o_strides,
+                             const int32_t* seqlens_k,
+                             float scale, int32_t causal, int32_t num_splits,
+                             void* workspace, size_t workspace_bytes,
+                             struct ihipStream_t* stream);
+
+/* Bytes of workspace mi_attn_decode needs for these sizes (0: none), and
+ * the number of key splits it will use; both 0 for invalid sizes. */
+MI_ATTN_API size_t mi_attn_decode_workspace_size(int32_t batch, int32_t hq, int32_t hkv,
+                                                 int32_t lq, int32_t lk, int32_t head_dim,
+                                                 int32_t num_splits);
+MI_ATTN_API int32_t mi_attn_decode_splits(int32_t batch, int32_t hq, int32_t hkv,
+                                          int32_t lq, int32_t lk, int32_t head_dim,
+                                          int32_t num_splits);
 
 /* Static, human-readable text for a status code (never NULL). */
 MI_ATTN_API const char* mi_attn_status_string(mi_attn_status_t status);

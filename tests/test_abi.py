@@ -28,7 +28,8 @@ def _header():
 def test_exports_every_declared_function():
     names = re.findall(r"MI_ATTN_API\s+[\w\s\*]+?\b(mi_attn_\w+)\s*\(",
                        _header())
-    assert set(names) == {"mi_attn_fwd", "mi_attn_fwd_select",
+    assert set(names) == {"mi_attn_fwd", "mi_attn_fwd_select", "mi_attn_decode",
+                          "mi_attn_decode_workspace_size", "mi_attn_decode_splits",
                           "mi_attn_status_string", "mi_attn_version",
                           "mi_attn_last_hip_error"}
     for n in names:
@@ -126,3 +127,49 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(mi.MiAttnError) as e:
         mi.mi_attn_fwd(q, q, q, q.clone())
     assert e.value.status == 6
+
+
+# ---------------------------------------------------------------------------
+# mi_attn_decode: rejected before any HIP call
+# ---------------------------------------------------------------------------
+
+def dcall(q=A, k=A * 2, v=A * 3, o=A * 4, lse=A * 5, in_dt=1, out_dt=1, b=2, hq=8,
+          hkv=2, lq=1, lk=4096, d=128, qs=None, ks=None, vs=None, os_=None, seq=None,
+          scale=0.1, causal=1, splits=0, ws=A * 16, ws_bytes=1 << 30):
+    ref = lambda s: None if s is None else ctypes.byref(s)
+    return mi.lib().mi_attn_decode(q, k, v, o, lse, in_dt, out_dt, b, hq, hkv, lq, lk, d,
+                                   ref(qs), ref(ks), ref(vs), ref(os_), seq, scale, causal,
+                                   splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(o=None), 1),
+    (dict(in_dt=2), 4), (dict(in_dt=0, out_dt=1), 4),
+    (dict(lq=33), 2), (dict(lq=-1), 2), (dict(hq=6, hkv=4), 2), (dict(b=-1), 2),
+    (dict(d=96), 5), (dict(scale=math.nan), 6), (dict(causal=3), 6),
+    (dict(splits=-1), 6), (dict(splits=70000), 6),
+    (dict(ws=None), 1),                    # several splits need a workspace
+    (dict(ws=A * 16 + 64), 3),             # not 256-byte aligned
+    (dict(ws_bytes=1000), 8),              # smaller than required
+    (dict(ks=Strides(0, 4096 * 128, 64)), 3),   # rows overlap
+    (dict(q=A + 8), 3),
+])
+def test_decode_rejected_before_any_hip_call(kw, code):
+    assert dcall(**kw) == code
+
+
+def test_decode_workspace_plan():
+    size = mi.mi_attn_decode_workspace_size
+    splits = mi.mi_attn_decode_splits
+    # one work-group per CU for 8 x 8 query groups, 4 heads x 1 row each
+    assert splits(8, 32, 8, 1, 8192, 128) == 4
+    assert size(8, 32, 8, 1, 8192, 128) >= 8 * 32 * 1 * 4 * (128 + 2) * 4
+    # a single split needs no workspace, and a short cache gets one split
+    assert size(1, 4, 1, 1, 100, 64) == 0 and splits(1, 4, 1, 1, 100, 64) == 1
+    # the caller's split count is capped so every split has keys
+    assert splits(1, 8, 8, 1, 1000, 64, 64) == 8
+    assert splits(1, 8, 8, 1, 1000, 64, 3) == 3
+    # invalid sizes give 0
+    assert size(1, 8, 3, 1, 100, 64) == 0 and splits(1, 8, 8, 40, 100, 64) == 0
+    # empty work is a no-op without any pointers
+    assert dcall(b=0, q=None, k=None, v=None, o=None, ws=None) == 0

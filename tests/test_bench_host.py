@@ -115,5 +115,6 @@ def test_metric_labels():
     assert labels["causal_b2h16"] == ("attn fwd TFLOP/s + % of fp16 MFMA peak, "
                                       "B2 H16 N2048 d64 causal")
     assert len(set(labels.values())) == len(labels)
+    assert labels["decode_gqa"].startswith("attn decode GB/s")
     assert "Hq32 Hkv8" in labels["gqa_causal"] and "causal" in labels["gqa_causal"]
     assert "Lq8192 Lk8192" in labels["long_8k"] and "bf16" in labels["long_8k"]

@@ -1,0 +1,166 @@
+"""GPU parity of mi_attn_decode (a few query rows against a long key/value
+cache, keys split across work-groups and merged by log-sum-exp) against the
+fp64 oracle.
+
+The oracle is the same materialised definition as for the forward pass:
+with Lq < Lk and causal masking it is bottom-right aligned (the new queries
+follow the cache, training-integration tutorial section 4.3), and a
+sequence's cache length seqlens_k[b] is taken by slicing its keys.  Same
+tolerances: output max-abs 1e-2, LSE max-abs 1e-3, rows with no visible key
+exactly O = 0 and LSE = -inf.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import compare, note
+
+pytestmark = pytest.mark.gpu
+
+F16, BF16 = torch.float16, torch.bfloat16
+
+
+def run_decode(q, k, v, seqlens=None, **kw):
+    import exact_attention_61_amd as mi
+    dev = torch.device("cuda", 0)
+    sl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32, device=dev)
+    o, lse = mi.decode(q.to(dev), k.to(dev), v.to(dev), seqlens_k=sl, **kw)
+    torch.cuda.synchronize()
+    return o.to("cpu", torch.float64).numpy(), lse.to("cpu", torch.float64).numpy()
+
+
+def oracle_decode(q, k, v, seqlens, scale, causal):
+    f64 = workloads.to_f64
+    qd, kd, vd = f64(q), f64(k), f64(v)
+    b = q.shape[0]
+    o = np.zeros(qd.shape)
+    lse = np.full(qd.shape[:3], -math.inf)
+    for i in range(b):
+        n = kd.shape[2] if seqlens is None else seqlens[i]
+        o[i:i + 1], lse[i:i + 1] = oracle.attention(qd[i:i + 1], kd[i:i + 1, :, :n],
+                                                    vd[i:i + 1, :, :n], scale=scale,
+                                                    causal=causal)
+    return o, lse
+
+
+def decode_case(b, hq, hkv, lq, lk, d, dtype, causal, splits=0, seqlens=None, seed=0,
+                scale=None, out_dtype=None):
+    q, k, v = workloads.make_dense(b, hq, hkv, lq, lk, d, dtype, seed)
+    o, lse = run_decode(q, k, v, seqlens, causal=causal, num_splits=splits, scale=scale,
+                        out_dtype=out_dtype)
+    o_ref, l_ref = oracle_decode(q, k, v, seqlens, scale, causal)
+    return compare(o, lse, o_ref, l_ref)
+
+
+@pytest.mark.parametrize("lq", [1, 2, 5, 16, 32])
+@pytest.mark.parametrize("lk", [1, 31, 33, 129, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_lengths(lq, lk, causal):
+    note(f"decode lq {lq} lk {lk} causal {causal}")
+    decode_case(2, 8, 2, lq, lk, 128, BF16, causal)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 7, 64])
+@pytest.mark.parametrize("d,dtype", [(64, F16), (128, BF16)])
+def test_decode_splits(splits, d, dtype):
+    note(f"decode splits {splits} d {d} {dtype}")
+    eo, el = decode_case(2, 16, 4, 3, 4100, d, dtype, True, splits=splits, seed=1)
+    note(f"  err_O {eo:.3e}  err_LSE {el:.3e}")
+
+
+def test_split_count_leaves_the_result_unchanged():
+    """Splitting the keys differently changes only roundings: each split
+    rounds its probabilities (fp16 here, 2^-12 relative) against its own
+    running max, and the fp32 sums are added in another order."""
+    note("decode split invariance")
+    q, k, v = workloads.make_dense(1, 8, 8, 4, 3000, 64, F16, seed=2)
+    outs = [run_decode(q, k, v, causal=True, num_splits=s, out_dtype=torch.float32)
+            for s in (1, 2, 5, 12)]
+    for o, lse in outs[1:]:
+        assert np.max(np.abs(o - outs[0][0])) <= 1e-4
+        assert np.max(np.abs(lse - outs[0][1])) <= 1e-5
+
+
+@pytest.mark.parametrize("hq,hkv,lq", [(4, 1, 1), (32, 8, 1), (32, 8, 16), (12, 12, 3),
+                                       (40, 5, 4), (33, 1, 2)])
+def test_decode_gqa_groups(hq, hkv, lq):
+    """Query heads of a kv head packed with the Lq positions into <= 32 rows
+    (several query groups per kv head when they do not fit)."""
+    note(f"decode gqa {hq}/{hkv} lq {lq}")
+    decode_case(2, hq, hkv, lq, 777, 64, BF16, True, seed=3)
+
+
+def test_decode_per_sequence_cache_lengths():
+    """seqlens_k gives each sequence its own cache length; sequences shorter
+    than Lq leave their first rows with no visible key (O = 0, LSE = -inf)."""
+    seqlens = [1000, 1, 0, 37, 4096, 3]
+    note(f"decode seqlens {seqlens}")
+    decode_case(6, 8, 2, 4, 4096, 128, F16, True, seqlens=seqlens, seed=4)
+    decode_case(6, 8, 2, 4, 4096, 64, BF16, False, seqlens=seqlens, seed=5, splits=5)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_decode_worked_example(dtype):
+    """Scores [0, ln 2] and values [1, 3] give 7/3 and LSE ln 3 (fusion notes,
+    section 3.1, example 5-6), here with the two keys in different splits."""
+    note(f"decode worked example {dtype}")
+    d = 64
+    lk = 512
+    q = torch.zeros(1, 1, 1, d, dtype=dtype)
+    q[..., 0] = 1
+    k = torch.zeros(1, 1, lk, d, dtype=dtype)
+    k[0, 0, 300, 0] = 1                 # score ln 2 in the second split
+    v = torch.zeros(1, 1, lk, d, dtype=dtype)
+    v[0, 0, 0] = 1                       # key 0: score 0, value 1
+    v[0, 0, 300] = 3
+    seq = [301]                          # keys 1..299 exist too: give them score -inf
+    kk = k.clone()
+    kk[0, 0, 1:300, 0] = -1e4            # exp(-1e4 ln 2 / ...) underflows to 0
+    o, lse = run_decode(q, kk, v, seq, scale=math.log(2.0), causal=False, num_splits=2,
+                        out_dtype=torch.float32)
+    assert np.allclose(o, 7.0 / 3.0, atol=1e-6, rtol=0)
+    assert abs(lse[0, 0, 0] - math.log(3.0)) <= 1e-6
+
+
+def test_decode_counters_reset_and_reuse():
+    """Every call leaves the workspace's arrival counters at zero, so one
+    workspace serves call after call."""
+    import exact_attention_61_amd as mi
+    note("decode workspace reuse")
+    dev = torch.device("cuda", 0)
+    b, hq, hkv, lq, lk, d, req = 2, 8, 2, 2, 3000, 128, 6
+    q, k, v = workloads.make_dense(b, hq, hkv, lq, lk, d, BF16, seed=6)
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    n = mi.mi_attn_decode_workspace_size(b, hq, hkv, lq, lk, d, req)
+    splits = mi.mi_attn_decode_splits(b, hq, hkv, lq, lk, d, req)
+    assert splits == req and n > 0
+    ws = torch.zeros(n, dtype=torch.uint8, device=dev)
+    o_ref, l_ref = oracle_decode(q, k, v, None, None, True)
+    # layout: partial outputs, partial (m, l), then one counter per query
+    # group (8 / 2 = 4 heads x 2 rows fit one group of 32 rows)
+    align = lambda x: (x + 255) // 256 * 256
+    rows = b * hq * lq * splits
+    off_cnt = align(rows * d * 4) + align(rows * 2 * 4)
+    groups = b * hkv * 1
+    for _ in range(3):
+        o, lse = mi.decode(qg, kg, vg, num_splits=req, workspace=ws)
+        torch.cuda.synchronize()
+        compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, l_ref)
+        cnt = ws[off_cnt:off_cnt + 4 * groups].view(torch.int32)
+        assert torch.count_nonzero(cnt).item() == 0
+
+
+@pytest.mark.parametrize("name", ["decode_gqa"])
+def test_decode_workload_full(name):
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make(name, seed=0)
+    note(f"decode workload {name} (full oracle)")
+    o, lse = run_decode(inp["q"], inp["k"], inp["v"], causal=w.causal, scale=w.scale)
+    o_ref, l_ref = oracle_decode(inp["q"], inp["k"], inp["v"], None, w.scale, w.causal)
+    eo, el = compare(o, lse, o_ref, l_ref)
+    note(f"  err_O {eo:.3e}  err_LSE {el:.3e}")

@@ -21,6 +21,10 @@ The five named workloads follow the shapes the pages use:
            (tutorial 2.3).
 * long_8k: B=1, H=16, L=8192, d=128, non-causal, bf16 (the L=8192, d=128
            sizing table of the fusion notes, section 3).
+* decode_gqa: one new token per sequence against an 8192-token key/value
+           cache: B=8, 32 query heads over 8 KV heads, d=128, bf16, causal
+           (bottom-right: the new token follows the cache, tutorial section
+           4.3); the GQA grouping of tutorial section 2.3.
 """
 
 import math
@@ -47,6 +51,7 @@ class Workload:
     scale: float
     varlen: bool = False
     len_range: tuple = field(default=(0, 0))   # varlen: inclusive [lo, hi]
+    decode: bool = False   # a few query rows against a key/value cache
 
 
 WORKLOADS = {
@@ -61,6 +66,8 @@ WORKLOADS = {
                            "bf16", "bf16", 1.0 / math.sqrt(128.0)),
     "long_8k": Workload("long_8k", 1, 16, 16, 8192, 8192, 128, False,
                         "bf16", "bf16", 1.0 / math.sqrt(128.0)),
+    "decode_gqa": Workload("decode_gqa", 8, 32, 8, 1, 8192, 128, True,
+                           "bf16", "bf16", 1.0 / math.sqrt(128.0), decode=True),
 }
 
 # The workload the benchmark headline is quoted on.
