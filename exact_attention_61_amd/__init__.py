@@ -11,6 +11,8 @@ Entry points mirror the C ABI of include/mi_attn.h:
   and the causal tile order chosen explicitly (tests and diagnostics);
 * mi_attn_decode(q, k, v, o, lse, ...) -- a few query rows against a long
   key/value cache, keys split across work-groups (needs a workspace);
+* mi_attn_decode_noalloc(q, k, v, o, lse, ...) -- the same with its scratch
+  in a static device array of the library (no allocation at all);
 * mi_attn_decode_workspace_size(...), mi_attn_decode_splits(...);
 * mi_attn_status_string(code), mi_attn_version(), mi_attn_last_hip_error();
 
@@ -73,6 +75,10 @@ def _load():
     lib.mi_attn_decode.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int,
                                    i32, i32, i32, i32, i32, i32, S, S, S, S, P,
                                    ctypes.c_float, i32, i32, P, ctypes.c_size_t, P]
+    lib.mi_attn_decode_noalloc.restype = ctypes.c_int
+    lib.mi_attn_decode_noalloc.argtypes = lib.mi_attn_decode.argtypes[:20] + [P]
+    lib.mi_attn_decode_noalloc_max_bytes.restype = ctypes.c_size_t
+    lib.mi_attn_decode_noalloc_max_bytes.argtypes = []
     lib.mi_attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.mi_attn_decode_workspace_size.argtypes = [i32] * 7
     lib.mi_attn_decode_splits.restype = i32
@@ -219,6 +225,15 @@ def mi_attn_decode_splits(batch, hq, hkv, lq, lk, head_dim, num_splits=0):
     return int(_lib.mi_attn_decode_splits(batch, hq, hkv, lq, lk, head_dim, num_splits))
 
 
+def mi_attn_decode_noalloc(q, k, v, o, lse=None, *, seqlens_k=None, causal=True,
+                           scale=None, num_splits=0, stream=None):
+    """mi_attn_decode with the library's static scratch instead of a
+    workspace: nothing is allocated.  Calls that overlap in time on one GPU
+    race (they share the scratch)."""
+    _decode_call(q, k, v, o, lse, seqlens_k, causal, scale, num_splits, None, stream,
+                 noalloc=True)
+
+
 def mi_attn_decode(q, k, v, o, lse=None, *, seqlens_k=None, causal=True, scale=None,
                    num_splits=0, workspace=None, stream=None):
     """Call mi_attn_decode on caller-provided tensors (one device).
@@ -229,6 +244,12 @@ def mi_attn_decode(q, k, v, o, lse=None, *, seqlens_k=None, causal=True, scale=N
     mi_attn_decode_workspace_size(...) bytes whose counters start at zero
     (torch.zeros), or None when that size is 0.
     """
+    _decode_call(q, k, v, o, lse, seqlens_k, causal, scale, num_splits, workspace, stream,
+                 noalloc=False)
+
+
+def _decode_call(q, k, v, o, lse, seqlens_k, causal, scale, num_splits, workspace, stream,
+                 noalloc):
     for t in (q, k, v, o, lse, seqlens_k, workspace):
         if t is not None and (not t.is_cuda or t.device != q.device):
             raise MiAttnError(6, "every tensor must be on q's GPU device")
@@ -248,14 +269,17 @@ def mi_attn_decode(q, k, v, o, lse=None, *, seqlens_k=None, causal=True, scale=N
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     qs, ks, vs, os_ = (_strides(t, "bhsd", False) for t in (q, k, v, o))
-    ws_ptr, ws_bytes = (None, 0) if workspace is None else (
-        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size())
-    st = _lib.mi_attn_decode(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-        _DTYPE_CODE[q.dtype], _DTYPE_CODE[o.dtype], bsz, hq, hkv, lq, lk, d,
-        ctypes.byref(qs), ctypes.byref(ks), ctypes.byref(vs), ctypes.byref(os_),
-        _ptr(seqlens_k), float(scale), int(bool(causal)), int(num_splits),
-        ws_ptr, ws_bytes, ctypes.c_void_p(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+            _DTYPE_CODE[q.dtype], _DTYPE_CODE[o.dtype], bsz, hq, hkv, lq, lk, d,
+            ctypes.byref(qs), ctypes.byref(ks), ctypes.byref(vs), ctypes.byref(os_),
+            _ptr(seqlens_k), float(scale), int(bool(causal)), int(num_splits))
+    if noalloc:
+        st = _lib.mi_attn_decode_noalloc(*args, ctypes.c_void_p(stream))
+    else:
+        ws_ptr, ws_bytes = (None, 0) if workspace is None else (
+            ctypes.c_void_p(workspace.data_ptr()),
+            workspace.numel() * workspace.element_size())
+        st = _lib.mi_attn_decode(*args, ws_ptr, ws_bytes, ctypes.c_void_p(stream))
     if st != 0:
         detail = f"hipError {mi_attn_last_hip_error()}" if st == 7 else ""
         raise MiAttnError(st, detail)

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/mi_attn.h"
 #include "common.hpp"
@@ -194,6 +195,61 @@ DecodePlan decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t lq, int32
     return pl;
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch of mi_attn_decode_noalloc: a file-scope device array, one
+// copy per GPU, reached through the address hipGetSymbolAddress gives on that
+// device (the array's name is only a host-side stand-in).  The first 64 KiB
+// are the arrival counters (one per query group, at most 16384 groups);
+// the partial results follow.  The counters are cleared once per device at
+// set-up and every call leaves them at zero.
+// ---------------------------------------------------------------------------
+
+constexpr size_t kScratchBytes = size_t(8) << 20;           // 8 MiB per GPU
+constexpr size_t kScratchCounterBytes = size_t(64) << 10;   // 16384 counters
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ void clear_words_kernel(int32_t* w, int n) {
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) w[i] = 0;
+}
+
+struct ScratchSlot {
+    std::once_flag once;
+    char* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The scratch address on the current device; on the first call for the
+// device its counter region is cleared by a fill kernel on `stream`.
+hipError_t scratch_on_current_device(hipStream_t stream, char** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&]() {
+        void* ptr = nullptr;
+        slot.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (slot.err != hipSuccess) return;
+        const int n = (int)(kScratchCounterBytes / 4);
+        hipLaunchKernelGGL(clear_words_kernel, dim3((n + 255) / 256), dim3(256), 0, stream,
+                           static_cast<int32_t*>(ptr), n);
+        slot.err = hipGetLastError();
+        if (slot.err == hipSuccess) slot.ptr = static_cast<char*>(ptr);
+    });
+    *out = slot.ptr;
+    return slot.err;
+}
+
+bool fits_scratch(const DecodePlan& pl, int32_t batch, int32_t hkv) {
+    const int64_t groups = (int64_t)batch * hkv * pl.nqg;
+    return groups * 4 <= (int64_t)kScratchCounterBytes &&
+           pl.off_cnt <= kScratchBytes - kScratchCounterBytes;
+}
+
 // Validation and launch of the decode path.  `workspace` (bytes) holds the
 // partial results and the arrival counters; the counters must be zero
 // before the first call and are zero again after every call.
@@ -204,7 +260,7 @@ mi_attn_status_t decode(const void* q, const void* k, const void* v, void* o, fl
                         const mi_attn_strides_t* v_strides, const mi_attn_strides_t* o_strides,
                         const int32_t* seqlens_k, float scale, int32_t causal,
                         int32_t num_splits, void* workspace, size_t workspace_bytes,
-                        struct ihipStream_t* stream) {
+                        struct ihipStream_t* stream, bool use_scratch = false) {
     if (in_dtype != MI_ATTN_F16 && in_dtype != MI_ATTN_BF16) return MI_ATTN_ERR_DTYPE;
     if (out_dtype != in_dtype && out_dtype != MI_ATTN_F32) return MI_ATTN_ERR_DTYPE;
     if (batch < 0 || lq < 0 || lk < 0 || hq < 1 || hkv < 1 || hq % hkv != 0)
@@ -233,10 +289,22 @@ mi_attn_status_t decode(const void* q, const void* k, const void* v, void* o, fl
         return MI_ATTN_ERR_LAYOUT;
     const DecodePlan pl = decode_plan(batch, hq, hkv, lq, lk, head_dim, num_splits);
     if ((int64_t)hkv * pl.nqg > 65535) return MI_ATTN_ERR_SHAPE;
-    if (pl.bytes > 0) {
+    if (use_scratch) {
+        if (pl.bytes > 0 && !fits_scratch(pl, batch, hkv)) return MI_ATTN_ERR_WORKSPACE;
+    } else if (pl.bytes > 0) {
         if (workspace == nullptr) return MI_ATTN_ERR_NULL;
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MI_ATTN_ERR_LAYOUT;
         if (workspace_bytes < pl.bytes) return MI_ATTN_ERR_WORKSPACE;
+    }
+    // the static scratch of this device (set up on the first call)
+    char* scratch_base = nullptr;
+    if (use_scratch && pl.bytes > 0) {
+        const hipError_t e = scratch_on_current_device(
+            reinterpret_cast<hipStream_t>(stream), &scratch_base);
+        if (e != hipSuccess) {
+            g_last_hip_error = (int32_t)e;
+            return MI_ATTN_ERR_HIP;
+        }
     }
 
     mi_attn::DecParams p{};
@@ -255,7 +323,12 @@ mi_attn_status_t decode(const void* q, const void* k, const void* v, void* o, fl
     p.scale_log2 = (float)std::fmax(std::fabs((double)scale) * 1.4426950408889634074, 1e-30);
     p.negate_q = scale < 0.0f ? 1 : 0;
     p.causal = causal;
-    if (pl.bytes > 0) {
+    if (pl.bytes > 0 && use_scratch) {
+        // counters in the fixed region at the front, the partials after it
+        p.counters = reinterpret_cast<int32_t*>(scratch_base);
+        p.part_o = reinterpret_cast<float*>(scratch_base + kScratchCounterBytes);
+        p.part_ml = reinterpret_cast<float*>(scratch_base + kScratchCounterBytes + pl.off_ml);
+    } else if (pl.bytes > 0) {
         char* ws = static_cast<char*>(workspace);
         p.part_o = reinterpret_cast<float*>(ws);
         p.part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
@@ -289,6 +362,23 @@ int32_t mi_attn_decode_splits(int32_t batch, int32_t hq, int32_t hkv, int32_t lq
         return 0;
     return decode_plan(batch, hq, hkv, lq, lk, head_dim, num_splits).splits;
 }
+
+mi_attn_status_t mi_attn_decode_noalloc(const void* q, const void* k, const void* v,
+                                        void* o, float* lse, mi_attn_dtype_t in_dtype,
+                                        mi_attn_dtype_t out_dtype, int32_t batch, int32_t hq,
+                                        int32_t hkv, int32_t lq, int32_t lk, int32_t head_dim,
+                                        const mi_attn_strides_t* q_strides,
+                                        const mi_attn_strides_t* k_strides,
+                                        const mi_attn_strides_t* v_strides,
+                                        const mi_attn_strides_t* o_strides,
+                                        const int32_t* seqlens_k, float scale, int32_t causal,
+                                        int32_t num_splits, struct ihipStream_t* stream) {
+    return decode(q, k, v, o, lse, in_dtype, out_dtype, batch, hq, hkv, lq, lk, head_dim,
+                  q_strides, k_strides, v_strides, o_strides, seqlens_k, scale, causal,
+                  num_splits, nullptr, 0, stream, true);
+}
+
+size_t mi_attn_decode_noalloc_max_bytes(void) { return kScratchBytes - kScratchCounterBytes; }
 
 mi_attn_status_t mi_attn_decode(const void* q, const void* k, const void* v, void* o,
                                 float* lse, mi_attn_dtype_t in_dtype,

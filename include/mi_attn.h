@@ -237,6 +237,36 @@ MI_ATTN_API mi_attn_status_t mi_attn_decode(const void* q, const void* k, const 
                              void* workspace, size_t workspace_bytes,
                              struct ihipStream_t* stream);
 
+/*
+ * mi_attn_decode_noalloc — mi_attn_decode for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the partial results and arrival counters live in a static
+ * device array of the library, 8 MiB per GPU, held until the process ends.
+ * It calls no hipMalloc, hipFree or other allocating routine.
+ *
+ * Sizes whose partial results need more than
+ * mi_attn_decode_noalloc_max_bytes() (8 MiB minus the 64 KiB counter
+ * region), or more than 16384 query groups (batch * hkv * query groups per
+ * kv head), return MI_ATTN_ERR_WORKSPACE before any HIP call.  The first
+ * call on a device clears the counters with a small kernel on its stream;
+ * every call leaves them at zero.  All calls on one GPU share the array:
+ * calls that overlap in time on one GPU (other streams, other threads)
+ * race and give wrong results.  Arguments otherwise as for mi_attn_decode.
+ */
+MI_ATTN_API mi_attn_status_t mi_attn_decode_noalloc(const void* q, const void* k,
+                             const void* v, void* o, float* lse,
+                             mi_attn_dtype_t in_dtype, mi_attn_dtype_t out_dtype,
+                             int32_t batch, int32_t hq, int32_t hkv,
+                             int32_t lq, int32_t lk, int32_t head_dim,
+                             const mi_attn_strides_t* q_strides,
+                             const mi_attn_strides_t* k_strides,
+                             const mi_attn_strides_t* v_strides,
+                             const mi_attn_strides_t* o_strides,
+                             const int32_t* seqlens_k,
+                             float scale, int32_t causal, int32_t num_splits,
+                             struct ihipStream_t* stream);
+MI_ATTN_API size_t mi_attn_decode_noalloc_max_bytes(void);
+
 /* Bytes of workspace mi_attn_decode needs for these sizes (0: none), and
  * the number of key splits it will use; both 0 for invalid sizes. */
 MI_ATTN_API size_t mi_attn_decode_workspace_size(int32_t batch, int32_t hq, int32_t hkv,

@@ -29,6 +29,7 @@ def test_exports_every_declared_function():
     names = re.findall(r"MI_ATTN_API\s+[\w\s\*]+?\b(mi_attn_\w+)\s*\(",
                        _header())
     assert set(names) == {"mi_attn_fwd", "mi_attn_fwd_select", "mi_attn_decode",
+                          "mi_attn_decode_noalloc", "mi_attn_decode_noalloc_max_bytes",
                           "mi_attn_decode_workspace_size", "mi_attn_decode_splits",
                           "mi_attn_status_string", "mi_attn_version",
                           "mi_attn_last_hip_error"}
@@ -173,3 +174,22 @@ def test_decode_workspace_plan():
     assert size(1, 8, 3, 1, 100, 64) == 0 and splits(1, 8, 8, 40, 100, 64) == 0
     # empty work is a no-op without any pointers
     assert dcall(b=0, q=None, k=None, v=None, o=None, ws=None) == 0
+
+
+def test_decode_noalloc_rejects_sizes_beyond_its_scratch():
+    """Rejected before any HIP call: partials past the static scratch, or
+    more query groups than counters."""
+    cap = mi.lib().mi_attn_decode_noalloc_max_bytes()
+    assert cap == (8 << 20) - (64 << 10)
+
+    def ncall(b, hq, hkv, lq, lk, d, splits):
+        return mi.lib().mi_attn_decode_noalloc(A, A * 2, A * 3, A * 4, A * 5, 1, 1, b, hq, hkv,
+                                               lq, lk, d, None, None, None, None, None,
+                                               0.1, 1, splits, None)
+    # 64 x 32 heads x 32 rows x 16 splits x 128 columns x 4 B = 64 MiB of partials
+    assert mi.mi_attn_decode_workspace_size(64, 32, 8, 32, 8192, 128, 16) > cap
+    assert ncall(64, 32, 8, 32, 8192, 128, 16) == 8
+    # 20000 sequences x 1 kv head: more query groups than counters
+    assert ncall(20000, 1, 1, 1, 4096, 64, 2) == 8
+    # validation errors come first, as for mi_attn_decode
+    assert ncall(1, 8, 3, 1, 100, 64, 0) == 2
