@@ -47,8 +47,11 @@ PEAK_HBM_GBS = 8000.0                            # MI355X HBM3E, per GPU
 # what the hot kernel is built from: its template, instantiations and flags
 KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_61_amd", *parts) for parts in
                (("csrc", "attn_fwd_mfma.hpp"), ("csrc", "attn_fwd_mfma_d64.hip"),
-                ("csrc", "attn_fwd_mfma_d128.hip"), ("csrc", "common.hpp"),
+                ("csrc", "attn_fwd_mfma_d128.hip"), ("csrc", "attn_decode.hip"),
+                ("csrc", "mfma_util.hpp"), ("csrc", "common.hpp"),
                 ("build.py",))]
+SIMDS = 4 * 256                                  # MI355X: 256 CUs x 4 SIMDs
+PEAK_CLOCK_HZ = 2.4e9                            # the clock the peaks are quoted at
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_mfma_counters.json")
 # What the headline line is quoted on (the workload's own label otherwise).
 HEADLINE_METRIC = ("attn fwd TFLOP/s + % of fp16 MFMA peak, B2 H16 N2048 d64 "
@@ -186,17 +189,81 @@ def _find(dirpath, suffix):
 
 
 def _per_dispatch(path, kernel_sub):
-    """Counter values per dispatch of the kernel: {counter: [values]}."""
-    per = {}
+    """Counter values per dispatch of the kernel: {counter: [values]}.
+    rocprofv3 can print a counter's row twice for one dispatch (same
+    correlation id, same value); such exact repeats are counted once."""
+    per, seen = {}, set()
     for r in _csv_rows(path):
         if kernel_sub not in r["Kernel_Name"]:
             continue
+        row = tuple(r.values())
+        if row in seen:
+            continue
+        seen.add(row)
         key = (r["Dispatch_Id"], r["Counter_Name"])
         per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
     out = {}
     for (_, name), val in per.items():
         out.setdefault(name, []).append(val)
     return out
+
+
+def read_bytes(d):
+    """HBM-side read bytes from the L2's fabric read requests by size."""
+    import statistics
+    m = lambda k: statistics.median(d[k])
+    return (32 * m("TCC_EA0_RDREQ_32B_sum") + 64 * m("TCC_EA0_RDREQ_64B_sum")
+            + 128 * m("TCC_EA0_RDREQ_128B_sum"))
+
+
+def write_bytes(d):
+    """Write bytes: 64-byte requests and 32-byte ones (the rest)."""
+    import statistics
+    m = lambda k: statistics.median(d[k])
+    w_all, w64 = m("TCC_EA0_WRREQ_sum"), m("TCC_EA0_WRREQ_64B_sum")
+    return 64 * w64 + 32 * (w_all - w64)
+
+
+READ_PMC = ("TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum "
+            "TCC_EA0_RDREQ_sum")
+WRITE_PMC = "TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum"
+MFMA_PMC = ("SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F16 "
+            "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES")
+
+
+def summarize_copy(dirpath):
+    """Markdown summary of the copy calibration: what the byte formulas
+    read for a plain device copy of known size."""
+    import statistics
+    rec = json.loads(open(os.path.join(dirpath, "copy.json")).read().strip()
+                     .splitlines()[-1]) if os.path.exists(
+        os.path.join(dirpath, "copy.json")) else {"copy_calibration_bytes": 256 << 20}
+    n = rec["copy_calibration_bytes"]
+    rd = _per_dispatch(_find(os.path.join(dirpath, "read"), "counter_collection.csv"),
+                       "copyBuffer")
+    wr = _per_dispatch(_find(os.path.join(dirpath, "write"), "counter_collection.csv"),
+                       "copyBuffer")
+    rb, wb = read_bytes(rd), write_bytes(wr)
+    cmd = "python3 bench.py --copy-calibration 256 --steps 3"
+    lines = [
+        "# Copy calibration of the HBM byte counters (256 MiB device-to-device copy)", "",
+        "Commands (repository root, MI355X, `TMPDIR=/tmp`):", "",
+        f"    rocprofv3 --pmc {READ_PMC} --output-format csv -d DIR/read -o r -- {cmd}",
+        f"    rocprofv3 --pmc {WRITE_PMC} --output-format csv -d DIR/write -o w -- {cmd}",
+        "    python bench.py --summarize-copy DIR", "",
+        "| quantity | per copy dispatch |", "|---|---|",
+        f"| dispatches of the copy kernel | {len(rd['TCC_EA0_RDREQ_sum'])} |",
+        f"| read requests 32 B / 64 B / 128 B | "
+        f"{statistics.median(rd['TCC_EA0_RDREQ_32B_sum']):.0f} / "
+        f"{statistics.median(rd['TCC_EA0_RDREQ_64B_sum']):.0f} / "
+        f"{statistics.median(rd['TCC_EA0_RDREQ_128B_sum']):.0f} |",
+        f"| read bytes (32·n32 + 64·n64 + 128·n128) | {rb / 2**20:.3f} MiB = {rb / n:.5f} x "
+        f"the copy's {n / 2**20:.0f} MiB |",
+        f"| write bytes (64·n64 + 32·(n − n64)) | {wb / 2**20:.3f} MiB = {wb / n:.5f} x |", "",
+        "Both formulas read the copy's size with no scale factor, so the kernels' "
+        "summaries use them unscaled.",
+    ]
+    print("\n".join(lines))
 
 
 def summarize_counters(dirpath, name, write_record):
@@ -210,11 +277,13 @@ def summarize_counters(dirpath, name, write_record):
     nbytes = algorithmic_bytes(w, inp)
     kern = "attn_decode_kernel" if w.decode else "attn_fwd_mfma_kernel"
     wl = f"--workload {name} "
+    run = f"-- python3 bench.py {wl}--steps 5 --warmup 2 --no-cpu-baseline"
     cmds = {
-        "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o t -- python3 bench.py {wl}--steps 50 --warmup 5 --no-cpu-baseline",
-        "read": f"rocprofv3 --pmc TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum TCC_EA0_RDREQ_sum --output-format csv -d DIR/read -o r -- python3 bench.py {wl}--steps 5 --warmup 2 --no-cpu-baseline",
-        "write": f"rocprofv3 --pmc TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum --output-format csv -d DIR/write -o w -- python3 bench.py {wl}--steps 5 --warmup 2 --no-cpu-baseline",
-        "mfma": f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES --output-format csv -d DIR/mfma -o m -- python3 bench.py {wl}--steps 5 --warmup 2 --no-cpu-baseline",
+        "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o t "
+                 f"-- python3 bench.py {wl}--steps 50 --warmup 5 --no-cpu-baseline",
+        "read": f"rocprofv3 --pmc {READ_PMC} --output-format csv -d DIR/read -o r {run}",
+        "write": f"rocprofv3 --pmc {WRITE_PMC} --output-format csv -d DIR/write -o w {run}",
+        "mfma": f"rocprofv3 --pmc {MFMA_PMC} --output-format csv -d DIR/mfma -o m {run}",
     }
     tr = [r for r in _csv_rows(_find(os.path.join(dirpath, "trace"), "kernel_trace.csv"))
           if kern in r["Kernel_Name"]]
@@ -223,17 +292,19 @@ def summarize_counters(dirpath, name, write_record):
     rd = _per_dispatch(_find(os.path.join(dirpath, "read"), "counter_collection.csv"), kern)
     wr = _per_dispatch(_find(os.path.join(dirpath, "write"), "counter_collection.csv"), kern)
     mf = _per_dispatch(_find(os.path.join(dirpath, "mfma"), "counter_collection.csv"), kern)
-    m = lambda d, k: statistics.mean(d[k])
+    m = lambda d, k: statistics.median(d[k])
     n32, n64, n128 = (m(rd, f"TCC_EA0_RDREQ_{x}B_sum") for x in (32, 64, 128))
     nall = m(rd, "TCC_EA0_RDREQ_sum")
-    read_b = 32 * n32 + 64 * n64 + 128 * n128
+    read_b = read_bytes(rd)
     w_all, w64 = m(wr, "TCC_EA0_WRREQ_sum"), m(wr, "TCC_EA0_WRREQ_64B_sum")
-    write_b = 64 * w64 + 32 * (w_all - w64)
+    write_b = write_bytes(wr)
     busy = m(mf, "SQ_VALU_MFMA_BUSY_CYCLES")
-    gui = m(mf, "GRBM_GUI_ACTIVE")
+    # GRBM_GUI_ACTIVE adds up the 8 XCDs' active cycles; it also counts
+    # the profiler's window around a short dispatch, so it is context only
+    gui = m(mf, "GRBM_GUI_ACTIVE") / 8
     mops = m(mf, "SQ_INSTS_VALU_MFMA_MOPS_F16") + m(mf, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
-    simds = 4 * 256
-    util_gui = busy / (gui * simds)
+    busy_peak = busy / (SIMDS * PEAK_CLOCK_HZ * t_avg)
+    busy_gui = busy / (SIMDS * gui)
     exec_flops = mops * 512
     h = kernel_hash()
     q, k, v = inp["q"], inp["k"], inp["v"]
@@ -246,6 +317,7 @@ def summarize_counters(dirpath, name, write_record):
         "`python exact_attention_61_amd/build.py`; each counter pass its own run):", "",
         *[f"    {c}" for c in cmds.values()],
         f"    python bench.py --summarize-counters DIR --workload {name}", "",
+        "Counter figures are medians over the kernel's dispatches in each run.", "",
         "| quantity | per launch |", "|---|---|",
         f"| kernel duration (trace, {len(dur)} dispatches) | mean {t_avg * 1e6:.2f} us, median "
         f"{statistics.median(dur) / 1e3:.2f} us, min {min(dur) / 1e3:.2f} us |",
@@ -259,7 +331,10 @@ def summarize_counters(dirpath, name, write_record):
         f"| write requests (64 B of them) | {w_all:.0f} ({w64:.0f}) |",
         f"| HBM write bytes | {write_b / 2**20:.2f} MiB = {write_b / (nbytes - in_b):.3f} x O+LSE "
         f"({(nbytes - in_b) / 2**20:.2f} MiB) |",
-        f"| MFMA busy cycles / (GRBM_GUI_ACTIVE x {simds} SIMDs) | {100 * util_gui:.1f} % |",
+        f"| MFMA busy: busy cycles / ({SIMDS} SIMDs x 2.4 GHz x mean duration) | "
+        f"{100 * busy_peak:.1f} % |",
+        f"| MFMA busy against GRBM_GUI_ACTIVE / 8 (context: includes the profiler's "
+        f"window) | {100 * busy_gui:.1f} % |",
         f"| executed MFMA flops (MOPS x 512) | {exec_flops / 1e9:.3f} GFLOP = "
         f"{exec_flops / flops:.3f} x algorithmic |", "",
         f"Kernel source sha256[:16] = {h}.",
@@ -277,7 +352,7 @@ def summarize_counters(dirpath, name, write_record):
             "hbm_bytes_per_launch": int(round(read_b + write_b)),
             "hbm_read_bytes_per_launch": int(round(read_b)),
             "hbm_write_bytes_per_launch": int(round(write_b)),
-            "mfma_busy": round(util_gui, 4),
+            "mfma_busy": round(busy_peak, 4),
             "kernel_us_mean": round(t_avg * 1e6, 3),
             "executed_mfma_flops": exec_flops,
             "source": f"profiles/{kern}_{name}_counters.md"}
@@ -299,6 +374,9 @@ def main():
     ap.add_argument("--summarize-counters", default=None, metavar="DIR",
                     help="print the Markdown summary of the rocprofv3 runs "
                          "under DIR (no GPU work)")
+    ap.add_argument("--summarize-copy", default=None, metavar="DIR",
+                    help="print the Markdown summary of the copy calibration's "
+                         "counter runs under DIR (no GPU work)")
     ap.add_argument("--write-record", action="store_true",
                     help="with --summarize-counters: update the counter "
                          "record under profiles/")
@@ -312,6 +390,9 @@ def main():
     if args.steps < 1:
         print("--steps must be at least 1", file=sys.stderr)
         sys.exit(2)
+    if args.summarize_copy:
+        summarize_copy(args.summarize_copy)
+        return
     if args.summarize_counters:
         import workloads
         summarize_counters(args.summarize_counters,

@@ -21,6 +21,7 @@ The five named workloads follow the shapes the pages use:
            (tutorial 2.3).
 * long_8k: B=1, H=16, L=8192, d=128, non-causal, bf16 (the L=8192, d=128
            sizing table of the fusion notes, section 3).
+* long_4k: long_8k at L=4096 (a check that HBM reads scale with L).
 * decode_gqa: one new token per sequence against an 8192-token key/value
            cache: B=8, 32 query heads over 8 KV heads, d=128, bf16, causal
            (bottom-right: the new token follows the cache, tutorial section
@@ -68,6 +69,9 @@ WORKLOADS = {
                         "bf16", "bf16", 1.0 / math.sqrt(128.0)),
     "decode_gqa": Workload("decode_gqa", 8, 32, 8, 1, 8192, 128, True,
                            "bf16", "bf16", 1.0 / math.sqrt(128.0), decode=True),
+    # long_8k at half the length: its HBM read bytes should halve with L
+    "long_4k": Workload("long_4k", 1, 16, 16, 4096, 4096, 128, False,
+                        "bf16", "bf16", 1.0 / math.sqrt(128.0)),
 }
 
 # The workload the benchmark headline is quoted on.
