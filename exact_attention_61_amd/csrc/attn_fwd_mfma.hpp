@@ -132,9 +132,15 @@ __device__ __forceinline__ lds16_t* ring() {
     return (lds16_t*)r;
 }
 
+// Rows and keys of one sequence: the first query row and key in the
+// tensors (packed input) and their counts.
+struct SeqSpan {
+    int q0, lq, k0, lk;
+};
+
 template <int D, typename Tin, typename Tout, bool CAUSAL>
 __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
-                                             int h, int b) {
+                                             int h, int b, SeqSpan span) {
     using L = Layout<D>;
     constexpr int BN = L::BN, KQ = L::KQ;
     constexpr int NKC = L::NKC, NKS = L::NKS, NDB = L::NDB;
@@ -163,14 +169,8 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         col = lane & 31;
     };
 
-    int q0 = 0, lq_b = p.lq, k0 = 0, lk_b = p.lk;
+    const int q0 = span.q0, lq_b = span.lq, k0 = span.k0, lk_b = span.lk;
     const bool packed = p.cu_q != nullptr;
-    if (packed) {
-        q0 = p.cu_q[b];
-        lq_b = p.cu_q[b + 1] - q0;
-        k0 = p.cu_k[b];
-        lk_b = p.cu_k[b + 1] - k0;
-    }
     const int row0 = qtile * kBM;
     if (row0 >= lq_b) return;            // uniform over the work-group
     // kv head h / group as a multiply-high by ceil(2^32 / group): exact for
@@ -986,11 +986,69 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     else finish(I1());
 }
 
+// Span of sequence b of a packed batch.
+__device__ __forceinline__ SeqSpan packed_span(const FwdParams& p, int b) {
+    const int q0 = p.cu_q[b], k0 = p.cu_k[b];
+    return SeqSpan{q0, p.cu_q[b + 1] - q0, k0, p.cu_k[b + 1] - k0};
+}
+
+// Work of a packed non-causal batch of at most 64 sequences, longest key
+// range first.  Every q-tile of sequence i visits the same ck_i key tiles,
+// so the (sequence, q-tile, head) items are ranked by ck_i, most first (ties
+// by sequence index, then q-tile, then head), and the work-group of linear
+// grid index r takes the item of rank r: the dispatcher, which hands out
+// work-groups in grid order as slots free up, then works heaviest first.
+// With two resident work-groups per CU, the second round of n_cu ranks is
+// taken in reverse (lightest of them first), so the pair a CU holds sums to
+// about the same work.  The lane of each sequence computes its rank and its
+// first item; the whole work-group derives the same answer.  Returns false
+// when the work-group has no item.
+template <int WG_PER_CU>
+__device__ __forceinline__ bool packed_item(const FwdParams& p, int& b, int& qtile, int& h,
+                                            SeqSpan& span) {
+    const int nb = p.batch;
+    const int lane = lane_id();
+    SeqSpan mine{0, 0, 0, 0};
+    if (lane < nb) mine = packed_span(p, lane);
+    const int nq = (mine.lq + kBM - 1) / kBM;       // q-tiles of this lane's sequence
+    const int ck = (mine.lk + 63) / 64;             // key tiles each of them visits
+    int rank = 0;
+    for (int j = 0; j < nb; ++j) {
+        const int cj = __builtin_amdgcn_readlane(ck, j);
+        rank += (cj > ck || (cj == ck && j < lane)) ? 1 : 0;
+    }
+    int first = 0, total = 0;                       // in q-tiles
+    for (int j = 0; j < nb; ++j) {
+        const int rj = __builtin_amdgcn_readlane(rank, j);
+        const int nj = __builtin_amdgcn_readlane(nq, j);
+        first += rj < rank ? nj : 0;
+        total += nj;
+    }
+    const int heads = p.hq;
+    const int n_items = total * heads;
+    int r = ((int)blockIdx.z * (int)gridDim.y + (int)blockIdx.y) * (int)gridDim.x +
+            (int)blockIdx.x;
+    if (WG_PER_CU == 2) {
+        const int lo = p.n_cu, hi2 = min(n_items, 2 * p.n_cu);
+        if (r >= lo && r < hi2) r = lo + (hi2 - 1 - r);
+    }
+    if (r >= n_items) return false;
+    const int it = r / heads;                       // q-tile rank
+    h = r - it * heads;
+    const uint64_t own = __builtin_amdgcn_ballot_w64(lane < nb && it >= first && it < first + nq);
+    b = (int)__builtin_ctzll(own);
+    qtile = it - __builtin_amdgcn_readlane(first, b);
+    span = SeqSpan{__builtin_amdgcn_readlane(mine.q0, b), __builtin_amdgcn_readlane(mine.lq, b),
+                   __builtin_amdgcn_readlane(mine.k0, b), __builtin_amdgcn_readlane(mine.lk, b)};
+    return true;
+}
+
 // Grid (x, y, z) = (query head, batch, item), dispatched x fastest, so that
 // consecutive work-groups take the same item of different heads (the
 // q-tiles of one head then share one XCD when the head count is a multiple
 // of the XCD count).
-//   non-causal: item = q-tile (packed batches: q-tile n-1-item).
+//   non-causal: item = q-tile; packed batches of at most 64 sequences are
+//     ranked by packed_item, larger ones take q-tile n-1-item.
 //   causal: q-tiles heaviest first; with `pair` 1 item t covers q-tiles
 //     n-1-t and t one after the other; with `pair` 2 the first half of the
 //     items goes heaviest-first and the second half lightest-first, so that
@@ -1004,19 +1062,27 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
                  "s"(p.q_sh), "s"(p.k_sh), "s"(p.v_sh), "s"(p.q_sr), "s"(p.k_sr),
                  "s"(p.v_sr), "s"(p.o_sh), "s"(p.o_sr), "s"(p.lq), "s"(p.lk),
                  "s"(p.group_magic), "s"(p.scale_log2));
-    const int h = (int)blockIdx.x;
-    const int b = (int)blockIdx.y;
+    int h = (int)blockIdx.x;
+    int b = (int)blockIdx.y;
     const int item = (int)blockIdx.z;
     if constexpr (!PAIRS) {
         // one q-tile per work-group: a straight-line body
         int t = item;
-        // packed batches: highest q-tile index first -- those q-tiles exist
-        // only for the longest sequences, whose work-groups are the heaviest
-        if (p.cu_q != nullptr) t = n_qtiles - 1 - item;
+        SeqSpan span{0, p.lq, 0, p.lk};
+        if (p.cu_q != nullptr) {
+            if (!CAUSAL && p.batch <= 64) {
+                if (!packed_item<Layout<D>::WG_PER_CU>(p, b, t, h, span)) return;
+            } else {
+                // highest q-tile index first: those q-tiles exist only for
+                // the longest sequences, whose work-groups are the heaviest
+                t = n_qtiles - 1 - item;
+                span = packed_span(p, b);
+            }
+        }
         if (CAUSAL)
             t = pair == 2 ? (item < n_qtiles / 2 ? n_qtiles - 1 - item : item - n_qtiles / 2)
                           : n_qtiles - 1 - item;
-        attend_qtile<D, Tin, Tout, CAUSAL>(p, t, h, b);
+        attend_qtile<D, Tin, Tout, CAUSAL>(p, t, h, b, span);
     } else {
         // causal, q-tiles n-1-item and item one after the other
         int tile[2] = {n_qtiles - 1 - item, -1};
@@ -1028,7 +1094,8 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
             // loop and kept live (spilled) across the whole key loop
             int hh = __builtin_amdgcn_readfirstlane(h), bb = __builtin_amdgcn_readfirstlane(b);
             asm volatile("" : "+s"(hh), "+s"(bb));
-            attend_qtile<D, Tin, Tout, CAUSAL>(p, tile[it], hh, bb);
+            const SeqSpan span = p.cu_q != nullptr ? packed_span(p, bb) : SeqSpan{0, p.lq, 0, p.lk};
+            attend_qtile<D, Tin, Tout, CAUSAL>(p, tile[it], hh, bb, span);
         }
     }
 }

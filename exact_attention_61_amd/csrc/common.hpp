@@ -29,6 +29,7 @@ struct FwdParams {
     int32_t negate_q;                // 1 when scale < 0 (fold the sign into q)
     int32_t causal;
     int32_t causal_pairs;            // causal q-tile order (0, 1, 2; -1 default)
+    int32_t n_cu;                    // compute units of the device
 };
 
 // Parameters of the decode kernel (attn_decode.hip): a few query rows per

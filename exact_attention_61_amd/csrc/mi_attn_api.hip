@@ -6,6 +6,7 @@
 // checks before any launch, an error code instead of a crash) and the
 // training tutorial's constraints (Hkv divides Hq, head_dim a multiple of 8).
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -37,6 +38,20 @@ mi_attn_strides_t default_strides(bool packed, int64_t heads, int64_t rows,
 }
 
 // Validation and launch shared by mi_attn_fwd and mi_attn_fwd_select.
+// Compute units of the current device (a scheduling hint for the kernels;
+// any positive value gives the same results).  Cached per device.
+static int current_device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 mi_attn_status_t forward(const void* q, const void* k, const void* v,
                          void* o, float* lse, mi_attn_dtype_t in_dtype,
                          mi_attn_dtype_t out_dtype, int32_t batch,
@@ -133,6 +148,7 @@ mi_attn_status_t forward(const void* q, const void* k, const void* v,
     p.negate_q = scale < 0.0f ? 1 : 0;
     p.causal = causal;
     p.causal_pairs = causal_order;
+    p.n_cu = current_device_cus();
 
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t err;

@@ -239,6 +239,30 @@ def test_varlen(causal, d, dtype):
     compare(o, lse, o_ref, l_ref)
 
 
+@pytest.mark.parametrize("nseq,causal", [(64, False), (65, False), (64, True)])
+def test_varlen_many_sequences(nseq, causal):
+    """Non-causal packed batches of up to 64 sequences are handed out
+    longest key range first (with ties, empty sequences and more work-groups
+    than two rounds of the CUs); larger or causal batches keep the grid
+    order.  Every (sequence, head, q-tile) must be computed exactly once."""
+    rng = np.random.default_rng(nseq)
+    lens_q = [int(x) for x in rng.integers(0, 300, size=nseq)]
+    lens_q[3] = lens_q[5] = 0
+    lens_q[7] = lens_q[9] = 257          # ties in length
+    lens_k = list(lens_q)
+    lens_k[11] = 0                       # rows with no key
+    note(f"varlen {nseq} sequences causal {causal}")
+    q, k, v, cq, ck = workloads.make_packed(lens_q, lens_k, 8, 2, 64, BF16, seed=12)
+    o, lse = run_gpu(q, k, v, cu_seqlens_q=cq, cu_seqlens_k=ck,
+                     max_seqlen_q=max(lens_q), max_seqlen_k=max(lens_k),
+                     causal=causal)
+    f64 = workloads.to_f64
+    o_ref, l_ref = oracle.attention(f64(q), f64(k), f64(v), causal=causal,
+                                    cu_seqlens_q=cq.numpy(),
+                                    cu_seqlens_k=ck.numpy())
+    compare(o, lse, o_ref, l_ref)
+
+
 def test_varlen_equals_per_sequence_dense_calls():
     lens = [33, 200, 129]
     note(f"varlen vs dense per sequence {lens}")
