@@ -1,4 +1,4 @@
-"""CPU oracle for the exact attention forward pass.
+"""CPU oracle for the exact attention forward pass and the rotary embedding.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package.  The product path (the HIP library
@@ -12,4 +12,11 @@ from .attention import (  # noqa: F401
     online_softmax_ul,
     online_softmax_normalised,
     row_probabilities,
+)
+from .rotary import (  # noqa: F401
+    inverse_frequencies,
+    pair_indices,
+    rotate,
+    rotate_dense,
+    rotate_packed,
 )

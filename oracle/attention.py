@@ -29,6 +29,10 @@ notes of the repository):
 * LSE is the natural log of sum_j exp(scale * q_i . k_j) over visible keys;
 * query head h uses KV head floor(h / G), G = Hq / Hkv (contiguous groups).
 
+Parity unpinned: the bottom-right causal rule for Lq != Lk is checked only
+against restatements of the same rule (the scalar brute force and the
+closed-form key counts); the pages fix no example of it.
+
 Layouts: dense tensors are [B, H, L, d]; packed variable-length tensors are
 [T, H, d] with cu_seqlens int arrays of length B + 1 (sequence b owns rows
 cu[b] .. cu[b+1]-1).  LSE is [B, Hq, Lq] (dense) or [Hq, Tq] (packed).
