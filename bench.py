@@ -73,9 +73,12 @@ def visible_pairs(w, lengths=None):
 
 
 def algorithmic_bytes(w, inp):
-    """Q, K, V read once and O, LSE written once."""
+    """Q, K, V read once and O, LSE written once (rotary: Q and K read and
+    written once)."""
     esz = {"f16": 2, "bf16": 2, "f32": 4}
     q, k, v = inp["q"], inp["k"], inp["v"]
+    if w.rotary:
+        return 2 * (q.numel() + k.numel()) * esz[w.in_dtype]
     n_in = (q.numel() + k.numel() + v.numel()) * esz[w.in_dtype]
     rows = q.numel() // w.d
     return n_in + rows * w.d * esz[w.out_dtype] + rows * 4
@@ -116,6 +119,9 @@ def metric_label(w):
     if w.decode:
         return (f"attn decode GB/s (HBM roofline), B{w.batch} Hq{w.hq} Hkv{w.hkv} "
                 f"Lq{w.lq} Lk{w.lk} d{w.d} {w.in_dtype}")
+    if w.rotary:
+        return (f"rotary embedding of Q and K in place, GB/s (HBM roofline), B{w.batch} "
+                f"Hq{w.hq} Hkv{w.hkv} L{w.lq} d{w.d} {w.in_dtype}")
     shape = (f"varlen B{w.batch} H{w.hq} max L{w.lq}" if w.varlen else
              f"B{w.batch} Hq{w.hq} Hkv{w.hkv} Lq{w.lq} Lk{w.lk}")
     return (f"attn fwd TFLOP/s + % of {w.in_dtype} MFMA peak, {shape} d{w.d}"
@@ -140,9 +146,38 @@ def blas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(w, inp, o_gpu, lse_gpu, flops, min_seconds=10.0):
+def rotary_cpu_baseline(w, inp, rotated, nbytes, min_seconds=10.0):
+    """Time the fp64 rotary oracle over the workload's Q and K (whole passes
+    until about min_seconds); also check the GPU's rotation of them."""
+    import numpy as np
+    import oracle
+    import workloads
+    f64 = workloads.to_f64
+    q, k = f64(inp["q"]), f64(inp["k"])
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        refs = [oracle.rotate_dense(x, w.d, 10000.0, False) for x in (q, k)]
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    rel = 2.0 ** -7 if w.in_dtype == "bf16" else 2.0 ** -10
+    excess = max(float(np.max(np.abs(g - r) - (rel * np.abs(r) + 1e-5)))
+                 for g, r in zip(rotated, refs))
+    err = max(float(np.max(np.abs(g - r))) for g, r in zip(rotated, refs))
+    base = {"value": round(nbytes * passes / dt / 1e9, 4), "unit": "GB/s",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"the whole {w.name} workload (Q and K), {passes} pass(es), "
+                      f"fp64 numpy, {dt:.2f} s"}
+    return base, {"max_abs_err": err, "pass": excess <= 0.0}
+
+
+def cpu_baseline(w, inp, o_gpu, lse_gpu, flops, nbytes, min_seconds=10.0):
     """Time the fp64 oracle over the whole workload (repeated until about
-    min_seconds have passed); also return parity of the GPU output."""
+    min_seconds have passed); also return parity of the GPU output.  The
+    rate is in the workload's unit: TFLOP/s, or GB/s of algorithmic bytes
+    for the HBM-bound decode."""
     import numpy as np
     import oracle
     import workloads
@@ -163,7 +198,11 @@ def cpu_baseline(w, inp, o_gpu, lse_gpu, flops, min_seconds=10.0):
     live = np.isfinite(l_ref)
     err_l = float(np.max(np.abs(lse_gpu[live] - l_ref[live])))
     dead_ok = bool(np.all(lse_gpu[~live] == -math.inf))
-    base = {"value": round(flops * passes / dt / 1e12, 6), "unit": "TFLOP/s",
+    if w.decode:
+        value, unit = round(nbytes * passes / dt / 1e9, 4), "GB/s"
+    else:
+        value, unit = round(flops * passes / dt / 1e12, 6), "TFLOP/s"
+    base = {"value": value, "unit": unit,
             "cores": blas_threads(), "kind": "oracle",
             "sample": f"the whole {w.name} workload, {passes} pass(es), fp64 "
                       f"numpy (S and P materialised per head in 1024-row "
@@ -273,9 +312,10 @@ def summarize_counters(dirpath, name, write_record):
     import workloads
     w = workloads.WORKLOADS[name]
     inp = workloads.make(name, seed=0)
-    flops = 4.0 * w.d * w.hq * visible_pairs(w, inp.get("lengths"))
+    flops = 0.0 if w.rotary else 4.0 * w.d * w.hq * visible_pairs(w, inp.get("lengths"))
     nbytes = algorithmic_bytes(w, inp)
-    kern = "attn_decode_kernel" if w.decode else "attn_fwd_mfma_kernel"
+    kern = ("attn_decode_kernel" if w.decode else "rotary_kernel" if w.rotary
+            else "attn_fwd_mfma_kernel")
     wl = f"--workload {name} "
     run = f"-- python3 bench.py {wl}--steps 5 --warmup 2 --no-cpu-baseline"
     cmds = {
@@ -422,8 +462,10 @@ def main():
     q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
     kw = dict(causal=w.causal, scale=w.scale)
     out_dtype = workloads.DTYPES[w.out_dtype]
-    o = torch.empty(q.shape, dtype=out_dtype, device=dev)
-    if w.varlen:
+    o = None if w.rotary else torch.empty(q.shape, dtype=out_dtype, device=dev)
+    if w.rotary:
+        lse = None
+    elif w.varlen:
         kw.update(cu_seqlens_q=inp["cu_seqlens_q"].to(dev),
                   cu_seqlens_k=inp["cu_seqlens_k"].to(dev),
                   max_seqlen_q=inp["max_seqlen_q"],
@@ -441,12 +483,25 @@ def main():
 
         def step():
             mi.mi_attn_decode(q, k, v, o, lse, workspace=workspace, **kw)
+    elif w.rotary:
+        # one rotation of fresh copies for the parity check, then the timed
+        # steps rotate q and k in place again and again
+        qr, kr = q.clone(), k.clone()
+        mi.mi_attn_rotary(qr, w.d)
+        mi.mi_attn_rotary(kr, w.d)
+        torch.cuda.synchronize()
+        rotated = [x.to("cpu", torch.float64).numpy() for x in (qr, kr)]
+        del qr, kr
+
+        def step():
+            mi.mi_attn_rotary(q, w.d)
+            mi.mi_attn_rotary(k, w.d)
     else:
         def step():
             mi.mi_attn_fwd(q, k, v, o, lse, **kw)
 
     lengths = inp.get("lengths")
-    flops = 4.0 * w.d * w.hq * visible_pairs(w, lengths)
+    flops = 0.0 if w.rotary else 4.0 * w.d * w.hq * visible_pairs(w, lengths)
     nbytes = algorithmic_bytes(w, inp)
 
     # warm-up (eager), with torch's peak-allocation counter reset first:
@@ -506,18 +561,24 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     counters = load_counter_record(name)
 
-    o_gpu = o.to("cpu", torch.float64).numpy()
-    lse_gpu = lse.to("cpu", torch.float64).numpy()
     base, parity = (None, None)
-    if not args.no_cpu_baseline:
-        base, parity = cpu_baseline(w, inp, o_gpu, lse_gpu, flops)
+    if w.rotary:
+        if not args.no_cpu_baseline:
+            base, parity = rotary_cpu_baseline(w, inp, rotated, nbytes)
+    else:
+        o_gpu = o.to("cpu", torch.float64).numpy()
+        lse_gpu = lse.to("cpu", torch.float64).numpy()
+        if not args.no_cpu_baseline:
+            base, parity = cpu_baseline(w, inp, o_gpu, lse_gpu, flops, nbytes)
 
-    if w.decode:
+    hbm_bound = w.decode or w.rotary
+    if hbm_bound:
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                     "traffic": None if counters is None else counters.get("hbm_bytes_per_launch"),
                     "mfma_busy": None if counters is None else counters.get("mfma_busy"),
-                    "algorithmic_bytes": nbytes, "kernel": "attn_decode_kernel"}
+                    "algorithmic_bytes": nbytes,
+                    "kernel": "rotary_kernel" if w.rotary else "attn_decode_kernel"}
     else:
         roofline = {"bound": "mfma", "achieved": round(tflops, 3),
                     "peak": peak_tf, "unit": "TFLOP/s",
@@ -528,8 +589,8 @@ def main():
                     "kernel": "attn_fwd_mfma_kernel"}
     rec = {
         "metric": metric_label(w),
-        "value": round(gbs, 1) if w.decode else round(tflops, 3),
-        "unit": "GB/s" if w.decode else "TFLOP/s",
+        "value": round(gbs, 1) if hbm_bound else round(tflops, 3),
+        "unit": "GB/s" if hbm_bound else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -544,12 +605,12 @@ def main():
                    "causal": w.causal, "varlen": w.varlen,
                    "in_dtype": w.in_dtype, "out_dtype": w.out_dtype,
                    "lengths": lengths},
-        "pct_of_peak": round(100.0 * (gbs / PEAK_HBM_GBS if w.decode else tflops / peak_tf), 2),
+        "pct_of_peak": round(100.0 * (gbs / PEAK_HBM_GBS if hbm_bound else tflops / peak_tf), 2),
         "algorithmic_flops": flops,
         "tflops": round(tflops, 3),
         # the common convention: 4*B*H*Lq*Lk*d, halved for causal
-        "flops_common_convention": (2.0 if w.causal else 4.0) * w.batch *
-        w.hq * w.lq * w.lk * w.d,
+        "flops_common_convention": 0.0 if w.rotary else (2.0 if w.causal else 4.0) *
+        w.batch * w.hq * w.lq * w.lk * w.d,
         "ms_per_step_median_batch": round(ms_median, 6),
         "batches": sizes,
         "ms_per_step_eager": round(ms_eager, 6),

@@ -83,6 +83,9 @@ def _load():
     lib.mi_attn_decode_workspace_size.argtypes = [i32] * 7
     lib.mi_attn_decode_splits.restype = i32
     lib.mi_attn_decode_splits.argtypes = [i32] * 7
+    lib.mi_attn_rotary.restype = ctypes.c_int
+    lib.mi_attn_rotary.argtypes = [P, ctypes.c_int, i32, i32, i32, i32, S, P, P,
+                                   ctypes.c_int64, i32, ctypes.c_double, i32, P]
     lib.mi_attn_status_string.restype = ctypes.c_char_p
     lib.mi_attn_status_string.argtypes = [ctypes.c_int]
     lib.mi_attn_version.restype = i32
@@ -302,6 +305,46 @@ def decode(q, k, v, *, seqlens_k=None, causal=True, scale=None, num_splits=0,
         mi_attn_decode(q, k, v, out, lse, seqlens_k=seqlens_k, causal=causal, scale=scale,
                        num_splits=num_splits, workspace=workspace)
     return out, lse
+
+
+def mi_attn_rotary(x, rotary_dim=None, *, base=10000.0, interleaved=False,
+                   position_offset=0, position_offsets=None, cu_seqlens=None,
+                   max_seqlen=None, layout="bhsd", stream=None):
+    """Rotary embedding of x in place (Q or K; one call per tensor).
+
+    Dense x is [B, H, L, d] ("bhsd") or [B, L, H, d] ("bshd"); packed x is
+    [T, H, d] with int32 cu_seqlens of length B + 1 and max_seqlen.  Row t of
+    sequence b sits at position position_offset + position_offsets[b] + t
+    (position_offsets: int32 [B] on the device, or None).  rotary_dim
+    defaults to d.  interleaved=False is the GPT-NeoX layout, True GPT-J.
+    """
+    packed = cu_seqlens is not None
+    for t in (position_offsets, cu_seqlens):
+        if t is not None and (not t.is_cuda or t.device != x.device):
+            raise MiAttnError(6, "every tensor must be on x's GPU device")
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise MiAttnError(3, "position_offsets / cu_seqlens must be contiguous int32")
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise MiAttnError(4, f"{x.dtype}")
+    d = x.shape[-1]
+    rd = d if rotary_dim is None else int(rotary_dim)
+    if packed:
+        bsz, heads, seqlen = cu_seqlens.numel() - 1, x.shape[1], int(max_seqlen)
+    elif layout == "bhsd":
+        bsz, heads, seqlen = x.shape[0], x.shape[1], x.shape[2]
+    else:
+        bsz, heads, seqlen = x.shape[0], x.shape[2], x.shape[1]
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    xs = _strides(x, layout, packed)
+    st = _lib.mi_attn_rotary(_ptr(x), _DTYPE_CODE[x.dtype], bsz, heads, seqlen, d,
+                             ctypes.byref(xs), _ptr(cu_seqlens), _ptr(position_offsets),
+                             int(position_offset), rd, float(base), int(bool(interleaved)),
+                             ctypes.c_void_p(stream))
+    if st != 0:
+        detail = f"hipError {mi_attn_last_hip_error()}" if st == 7 else ""
+        raise MiAttnError(st, detail)
+    return x
 
 
 def _check_cu(cu, max_len, rows):

@@ -60,6 +60,22 @@ struct DecParams {
     int32_t* counters;               // [B, hkv, nqg] arrivals, zero between calls
 };
 
+// Parameters of the rotary-embedding kernel (rotary.hip).  x is rotated in
+// place; row t of sequence b sits at position offset + offsets[b] + t.
+// Pair k (k < rotary_dim / 2) turns by position * freq_pi[k] half-turns
+// (freq_pi[k] = base^(-2k / rotary_dim) / pi, computed in double on the host).
+struct RopeParams {
+    void* x;
+    const int32_t* cu_seqlens;       // packed x [T, H, d], or null (dense)
+    const int32_t* offsets;          // per-sequence position offsets, or null
+    int64_t sb, sh, sr;              // element strides (batch unused when packed)
+    int32_t batch, heads, seqlen;    // seqlen: rows per sequence (packed: the maximum)
+    int32_t rotary_dim;              // a multiple of 16, <= head dim
+    int32_t interleaved;             // 0: pairs (k, k + rd/2); 1: pairs (2k, 2k + 1)
+    int64_t offset;
+    double freq_pi[128];
+};
+
 // Storage tags for the element types (16-bit values are kept as raw bits).
 struct f16_t { uint16_t bits; };
 struct bf16_t { uint16_t bits; };
@@ -112,5 +128,6 @@ hipError_t launch_mfma_d128(const FwdParams& p, int in_dtype, int out_dtype,
                            hipStream_t stream);
 hipError_t launch_decode(const DecParams& p, int in_dtype, int out_dtype, int head_dim,
                          hipStream_t stream);
+hipError_t launch_rotary(const RopeParams& p, int dtype, hipStream_t stream);
 
 }  // namespace mi_attn

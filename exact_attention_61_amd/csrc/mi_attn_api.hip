@@ -37,7 +37,6 @@ mi_attn_strides_t default_strides(bool packed, int64_t heads, int64_t rows,
     return mi_attn_strides_t{heads * rows * d, rows * d, d};
 }
 
-// Validation and launch shared by mi_attn_fwd and mi_attn_fwd_select.
 // Compute units of the current device (a scheduling hint for the kernels;
 // any positive value gives the same results).  Cached per device.
 static int current_device_cus() {
@@ -52,6 +51,7 @@ static int current_device_cus() {
     return n;
 }
 
+// Validation and launch shared by mi_attn_fwd and mi_attn_fwd_select.
 mi_attn_status_t forward(const void* q, const void* k, const void* v,
                          void* o, float* lse, mi_attn_dtype_t in_dtype,
                          mi_attn_dtype_t out_dtype, int32_t batch,
@@ -446,6 +446,52 @@ mi_attn_status_t mi_attn_fwd_select(const void* q, const void* k, const void* v,
                    head_dim, q_strides, k_strides, v_strides, o_strides,
                    cu_seqlens_q, cu_seqlens_k, scale, causal, stream,
                    (int32_t)kernel, causal_order);
+}
+
+mi_attn_status_t mi_attn_rotary(void* x, mi_attn_dtype_t dtype, int32_t batch,
+                                int32_t heads, int32_t seqlen, int32_t head_dim,
+                                const mi_attn_strides_t* strides, const int32_t* cu_seqlens,
+                                const int32_t* position_offsets, int64_t position_offset,
+                                int32_t rotary_dim, double base, int32_t interleaved,
+                                struct ihipStream_t* stream) {
+    if (dtype != MI_ATTN_F16 && dtype != MI_ATTN_BF16) return MI_ATTN_ERR_DTYPE;
+    if (batch < 0 || heads < 1 || seqlen < 0 || head_dim < 1) return MI_ATTN_ERR_SHAPE;
+    if (batch > 65535 || heads > 65535 * 4) return MI_ATTN_ERR_SHAPE;   // grid y and z
+    if (rotary_dim < 16 || rotary_dim % 16 != 0 || rotary_dim > head_dim || rotary_dim > 256)
+        return MI_ATTN_ERR_UNSUPPORTED;
+    if (!std::isfinite(base) || base <= 0.0) return MI_ATTN_ERR_ARG;
+    if (interleaved != 0 && interleaved != 1) return MI_ATTN_ERR_ARG;
+    if (batch == 0 || seqlen == 0) return MI_ATTN_OK;
+    if (x == nullptr) return MI_ATTN_ERR_NULL;
+    const bool packed = cu_seqlens != nullptr;
+    const mi_attn_strides_t xs = strides ? *strides : default_strides(packed, heads, seqlen, head_dim);
+    if (!stride_ok(xs) || !aligned16(x)) return MI_ATTN_ERR_LAYOUT;
+    // rows and heads may not overlap (a thread writes its features of every head)
+    if ((seqlen > 1 || packed) && xs.row < head_dim) return MI_ATTN_ERR_LAYOUT;
+    if (heads > 1 && xs.head < head_dim) return MI_ATTN_ERR_LAYOUT;
+
+    mi_attn::RopeParams p{};
+    p.x = x;
+    p.cu_seqlens = cu_seqlens;
+    p.offsets = position_offsets;
+    p.sb = xs.batch; p.sh = xs.head; p.sr = xs.row;
+    p.batch = batch;
+    p.heads = heads;
+    p.seqlen = seqlen;
+    p.rotary_dim = rotary_dim;
+    p.interleaved = interleaved;
+    p.offset = position_offset;
+    // pair k turns by base^(-2k / rd) radians per position, i.e.
+    // base^(-2k / rd) / pi half-turns
+    const double lb = std::log(base);
+    for (int k2 = 0; k2 < rotary_dim / 2; ++k2)
+        p.freq_pi[k2] = std::exp(-2.0 * k2 / rotary_dim * lb) / 3.14159265358979323846;
+    const hipError_t err = mi_attn::launch_rotary(p, (int)dtype, reinterpret_cast<hipStream_t>(stream));
+    if (err != hipSuccess) {
+        g_last_hip_error = (int32_t)err;
+        return MI_ATTN_ERR_HIP;
+    }
+    return MI_ATTN_OK;
 }
 
 const char* mi_attn_status_string(mi_attn_status_t status) {

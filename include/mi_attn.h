@@ -276,6 +276,49 @@ MI_ATTN_API int32_t mi_attn_decode_splits(int32_t batch, int32_t hq, int32_t hkv
                                           int32_t lq, int32_t lk, int32_t head_dim,
                                           int32_t num_splits);
 
+/*
+ * mi_attn_rotary -- rotary position embedding of Q or K, in place.
+ *
+ * The "Training integration" tutorial, section 4 (4.1-4.3): the rotary
+ * embedding applied to Q and K before attention, with a rotary dimension, a
+ * base frequency (10000 in the tutorial), the GPT-NeoX layout or the GPT-J
+ * layout, and a position offset for generation with a KV cache (the new
+ * tokens' positions start at the cache length).  Pair k (k < rotary_dim/2) of
+ * a row at position p turns by a = p * base^(-2k / rotary_dim):
+ * (x, y) -> (x cos a - y sin a, x sin a + y cos a).  interleaved = 0
+ * (GPT-NeoX): pair k is features (k, k + rotary_dim/2); interleaved = 1
+ * (GPT-J): features (2k, 2k + 1).  Features rotary_dim .. head_dim-1 are
+ * not touched.  The xPos scaling of section 4.4 is not provided.
+ *
+ * x          dense [batch, heads, seqlen, head_dim] through strides (NULL:
+ *            contiguous), or packed [T, heads, head_dim] when cu_seqlens
+ *            (device int32 [batch + 1]) is given; seqlen is then the longest
+ *            sequence.  F16 or BF16; rotated in fp32 and rounded back to
+ *            nearest even.
+ * positions  row t of sequence b sits at position_offset +
+ *            position_offsets[b] + t (position_offsets: device int32
+ *            [batch], or NULL for 0).
+ * rotary_dim a multiple of 16, at most head_dim and 256.
+ * stream     hipStream_t to enqueue on (NULL: default stream).
+ *
+ * Ownership: the caller owns x, cu_seqlens and position_offsets; nothing is
+ * retained.  Errors: a dtype other than F16/BF16 -> MI_ATTN_ERR_DTYPE; a
+ * negative size or batch > 65535 -> MI_ATTN_ERR_SHAPE; an unsupported
+ * rotary_dim -> MI_ATTN_ERR_UNSUPPORTED; base not finite and positive or
+ * interleaved not 0/1 -> MI_ATTN_ERR_ARG; x not 16-byte aligned, strides
+ * not multiples of 8 elements, or rows/heads that overlap ->
+ * MI_ATTN_ERR_LAYOUT; all checked before any HIP call.  batch or seqlen 0
+ * is a no-op.
+ */
+MI_ATTN_API mi_attn_status_t mi_attn_rotary(void* x, mi_attn_dtype_t dtype, int32_t batch,
+                                            int32_t heads, int32_t seqlen, int32_t head_dim,
+                                            const mi_attn_strides_t* strides,
+                                            const int32_t* cu_seqlens,
+                                            const int32_t* position_offsets,
+                                            int64_t position_offset, int32_t rotary_dim,
+                                            double base, int32_t interleaved,
+                                            struct ihipStream_t* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 MI_ATTN_API const char* mi_attn_status_string(mi_attn_status_t status);
 

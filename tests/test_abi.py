@@ -31,7 +31,7 @@ def test_exports_every_declared_function():
     assert set(names) == {"mi_attn_fwd", "mi_attn_fwd_select", "mi_attn_decode",
                           "mi_attn_decode_noalloc", "mi_attn_decode_noalloc_max_bytes",
                           "mi_attn_decode_workspace_size", "mi_attn_decode_splits",
-                          "mi_attn_status_string", "mi_attn_version",
+                          "mi_attn_rotary", "mi_attn_status_string", "mi_attn_version",
                           "mi_attn_last_hip_error"}
     for n in names:
         assert hasattr(mi.lib(), n), n
@@ -157,6 +157,34 @@ def dcall(q=A, k=A * 2, v=A * 3, o=A * 4, lse=A * 5, in_dt=1, out_dt=1, b=2, hq=
 ])
 def test_decode_rejected_before_any_hip_call(kw, code):
     assert dcall(**kw) == code
+
+
+def rcall(x=A, dt=1, b=2, h=4, l=100, d=128, xs=None, cu=None, offs=None, off=0, rd=128,
+          base=10000.0, inter=0):
+    ref = lambda s: None if s is None else ctypes.byref(s)
+    return mi.lib().mi_attn_rotary(x, dt, b, h, l, d, ref(xs), cu, offs, off, rd, base, inter,
+                                   None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(dt=2), 4), (dict(dt=-1), 4),
+    (dict(b=-1), 2), (dict(h=0), 2), (dict(l=-1), 2), (dict(d=0), 2), (dict(b=70000), 2),
+    (dict(h=65535 * 4 + 1), 2),
+    (dict(rd=0), 5), (dict(rd=8), 5), (dict(rd=24), 5), (dict(rd=144), 5),
+    (dict(d=512, rd=272), 5),
+    (dict(base=0.0), 6), (dict(base=-2.0), 6), (dict(base=math.nan), 6),
+    (dict(base=math.inf), 6), (dict(inter=2), 6),
+    (dict(x=A + 8), 3), (dict(xs=Strides(0, 128, 60)), 3),      # row stride not 8k
+    (dict(xs=Strides(0, 64, 512)), 3),                            # heads overlap
+    (dict(xs=Strides(0, 128 * 100, 64)), 3),                      # rows overlap
+])
+def test_rotary_rejected_before_any_hip_call(kw, code):
+    assert rcall(**kw) == code
+
+
+def test_rotary_empty_is_noop():
+    assert rcall(x=None, b=0) == 0
+    assert rcall(x=None, l=0) == 0
 
 
 def test_decode_workspace_plan():

@@ -78,11 +78,12 @@ def test_more_than_one_gpu_is_refused():
 
 
 @pytest.mark.gpu
-def test_bench_json_line_on_gpu():
-    """bench.py end to end on the tiny workload: one JSON line with the
-    contract's fields, a roofline entry and a passing parity record."""
+@pytest.mark.parametrize("name,bound", [("tiny", "mfma"), ("rotary_gqa", "hbm")])
+def test_bench_json_line_on_gpu(name, bound):
+    """bench.py end to end: one JSON line with the contract's fields, a
+    roofline entry and a passing parity record."""
     import json
-    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny",
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", name,
                           "--steps", "3", "--warmup", "1"],
                          capture_output=True, text=True, timeout=300)
     assert res.returncode == 0, res.stderr[-2000:]
@@ -92,9 +93,10 @@ def test_bench_json_line_on_gpu():
                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
                 "roofline", "cpu_baseline"):
         assert key in rec, key
-    assert rec["n_gpus"] == 1 and rec["steps"] == 3 and rec["config"]["workload"] == "tiny"
+    assert rec["n_gpus"] == 1 and rec["steps"] == 3 and rec["config"]["workload"] == name
     roof = rec["roofline"]
-    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s"
+    assert roof["bound"] == bound and roof["unit"] == ("TFLOP/s" if bound == "mfma" else "GB/s")
+    assert rec["unit"] == roof["unit"] and rec["cpu_baseline"]["unit"] == roof["unit"]
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert rec["cpu_baseline"]["kind"] == "oracle" and rec["cpu_baseline"]["cores"] >= 1
     assert rec["parity"]["pass"]

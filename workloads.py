@@ -22,6 +22,9 @@ The five named workloads follow the shapes the pages use:
 * long_8k: B=1, H=16, L=8192, d=128, non-causal, bf16 (the L=8192, d=128
            sizing table of the fusion notes, section 3).
 * long_4k: long_8k at L=4096 (a check that HBM reads scale with L).
+* rotary_gqa: the rotary embedding (tutorial section 4, GPT-NeoX layout,
+           rotary dimension = head dimension, base 10000) of the gqa_causal
+           Q and K, in place.
 * decode_gqa: one new token per sequence against an 8192-token key/value
            cache: B=8, 32 query heads over 8 KV heads, d=128, bf16, causal
            (bottom-right: the new token follows the cache, tutorial section
@@ -53,6 +56,7 @@ class Workload:
     varlen: bool = False
     len_range: tuple = field(default=(0, 0))   # varlen: inclusive [lo, hi]
     decode: bool = False   # a few query rows against a key/value cache
+    rotary: bool = False   # the rotary embedding of Q and K, in place
 
 
 WORKLOADS = {
@@ -69,6 +73,8 @@ WORKLOADS = {
                         "bf16", "bf16", 1.0 / math.sqrt(128.0)),
     "decode_gqa": Workload("decode_gqa", 8, 32, 8, 1, 8192, 128, True,
                            "bf16", "bf16", 1.0 / math.sqrt(128.0), decode=True),
+    "rotary_gqa": Workload("rotary_gqa", 1, 32, 8, 4096, 4096, 128, False,
+                           "bf16", "bf16", 1.0, rotary=True),
     # long_8k at half the length: its HBM read bytes should halve with L
     "long_4k": Workload("long_4k", 1, 16, 16, 4096, 4096, 128, False,
                         "bf16", "bf16", 1.0 / math.sqrt(128.0)),
