@@ -1,4 +1,5 @@
-"""CPU oracle for the exact attention forward pass and the rotary embedding.
+"""CPU oracle for the exact attention forward pass (with or without dropout)
+and the rotary embedding.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package.  The product path (the HIP library
@@ -19,4 +20,10 @@ from .rotary import (  # noqa: F401
     rotate,
     rotate_dense,
     rotate_packed,
+)
+from .dropout import (  # noqa: F401
+    attention_dropout,
+    drop_threshold,
+    keep_mask,
+    philox4x32_10,
 )
