@@ -69,6 +69,9 @@ def _load():
     lib.mi_attn_fwd.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int,
                                 i32, i32, i32, i32, i32, i32, S, S, S, S, P, P,
                                 ctypes.c_float, i32, P]
+    lib.mi_attn_fwd_dropout.restype = ctypes.c_int
+    lib.mi_attn_fwd_dropout.argtypes = lib.mi_attn_fwd.argtypes[:-1] + [
+        ctypes.c_double, ctypes.c_uint64, P]
     lib.mi_attn_fwd_select.restype = ctypes.c_int
     lib.mi_attn_fwd_select.argtypes = lib.mi_attn_fwd.argtypes + [ctypes.c_int, i32]
     lib.mi_attn_decode.restype = ctypes.c_int
@@ -168,8 +171,20 @@ def mi_attn_fwd_select(q, k, v, o, lse=None, *, kernel=MI_ATTN_KERNEL_MFMA,
           (int(kernel), int(causal_order)))
 
 
+def mi_attn_fwd_dropout(q, k, v, o, lse=None, *, dropout_p, seed, causal=False,
+                        scale=None, cu_seqlens_q=None, cu_seqlens_k=None,
+                        max_seqlen_q=None, max_seqlen_k=None, layout="bhsd",
+                        stream=None):
+    """mi_attn_fwd with dropout on the probabilities: each kept with
+    probability 1 - dropout_p (then scaled by 1 / (1 - dropout_p)), the mask
+    drawn from Philox4x32-10 keyed by the 64-bit seed."""
+    _call(q, k, v, o, lse, causal, scale, cu_seqlens_q, cu_seqlens_k,
+          max_seqlen_q, max_seqlen_k, layout, stream, None,
+          dropout=(float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF))
+
+
 def _call(q, k, v, o, lse, causal, scale, cu_seqlens_q, cu_seqlens_k,
-          max_seqlen_q, max_seqlen_k, layout, stream, select):
+          max_seqlen_q, max_seqlen_k, layout, stream, select, dropout=None):
     packed = cu_seqlens_q is not None or cu_seqlens_k is not None
     for t in (q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k):
         if t is not None and (not t.is_cuda or t.device != q.device):
@@ -206,7 +221,9 @@ def _call(q, k, v, o, lse, causal, scale, cu_seqlens_q, cu_seqlens_k,
             ctypes.byref(qs), ctypes.byref(ks), ctypes.byref(vs),
             ctypes.byref(os_), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
             float(scale), int(bool(causal)), ctypes.c_void_p(stream))
-    if select is None:
+    if dropout is not None:
+        st = _lib.mi_attn_fwd_dropout(*args[:-1], dropout[0], dropout[1], args[-1])
+    elif select is None:
         st = _lib.mi_attn_fwd(*args)
     else:
         st = _lib.mi_attn_fwd_select(*args, *select)
@@ -363,10 +380,11 @@ def _check_cu(cu, max_len, rows):
 def forward(q, k, v, *, causal=False, scale=None, cu_seqlens_q=None,
             cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
             out_dtype=None, layout="bhsd", return_lse=True, kernel=None,
-            causal_order=None):
+            causal_order=None, dropout_p=0.0, seed=0):
     """Allocate out (and lse) and run mi_attn_fwd; returns (out, lse).
 
-    kernel / causal_order (optional) go through mi_attn_fwd_select instead.
+    kernel / causal_order (optional) go through mi_attn_fwd_select instead;
+    dropout_p > 0 goes through mi_attn_fwd_dropout with the given seed.
     """
     packed = cu_seqlens_q is not None or cu_seqlens_k is not None
     out_dtype = q.dtype if out_dtype is None else out_dtype
@@ -384,7 +402,11 @@ def forward(q, k, v, *, causal=False, scale=None, cu_seqlens_q=None,
               cu_seqlens_k=cu_seqlens_k, max_seqlen_q=max_seqlen_q,
               max_seqlen_k=max_seqlen_k, layout=layout)
     with torch.cuda.device(q.device):
-        if kernel is None and causal_order is None:
+        if dropout_p:
+            if kernel is not None or causal_order is not None:
+                raise MiAttnError(6, "dropout runs the default kernel and order")
+            mi_attn_fwd_dropout(q, k, v, out, lse, dropout_p=dropout_p, seed=seed, **kw)
+        elif kernel is None and causal_order is None:
             mi_attn_fwd(q, k, v, out, lse, **kw)
         else:
             mi_attn_fwd_select(

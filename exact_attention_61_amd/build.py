@@ -39,6 +39,7 @@ HIPCC_FLAGS = [
 # in AGPRs would cost one copy instruction per score to reach the softmax.
 FILE_FLAGS = {
     "attn_fwd_mfma_d64.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+    "attn_fwd_mfma_drop_d64.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -132,13 +132,34 @@ __device__ __forceinline__ lds16_t* ring() {
     return (lds16_t*)r;
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
+// as easy as 1, 2, 3", SC 2011) on counter c with key (k0, k1): each round
+// multiplies words 0 and 2 by two constants and mixes the halves of the
+// products with the other words and the key; the key gains the Weyl
+// increments between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)c[0] * 0xD2511F53u;
+        const uint64_t p1 = (uint64_t)c[2] * 0xCD9E8D57u;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+        c[1] = (uint32_t)p1;
+        c[3] = (uint32_t)p0;
+        c[0] = n0;
+        c[2] = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+}
+
 // Rows and keys of one sequence: the first query row and key in the
 // tensors (packed input) and their counts.
 struct SeqSpan {
     int q0, lq, k0, lk;
 };
 
-template <int D, typename Tin, typename Tout, bool CAUSAL>
+template <int D, typename Tin, typename Tout, bool CAUSAL, bool DROP>
 __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                                              int h, int b, SeqSpan span) {
     using L = Layout<D>;
@@ -362,6 +383,8 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 #pragma unroll
         for (int db = 0; db < NDB; ++db) vf[db][c] = u32x4_t{0u, 0u, 0u, 0u};
     }
+    // with dropout every step reads the low part of the previous P
+    if constexpr (Mma<Tin>::kSplit && DROP) clear_p_lo();
 
     // Per-lane element offsets of the wave's fragments in a stage, opaque to
     // the optimiser (re-pinned after every step's barrier): every fragment
@@ -400,6 +423,21 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 if (8 * (e >> 2) + (e & 3) > lim) s_cur[rb][e] = -__builtin_inff();
         }
     };
+    // With dropout, bf16 P is split into hi + lo on every tile: the output
+    // is normalised by the fp32 sums of the probabilities before dropout,
+    // so the rounding of P does not cancel as it does with the rounded sums.
+    constexpr bool kSplitAll = Mma<Tin>::kSplit && DROP;
+    // Dropout mask of part g4 (scores 4 g4 .. 4 g4 + 3 of row block rb) of
+    // tile kt: keys kt*BN + 32 kq + 4 hi + 8 g4 + i, i = 0..3, one Philox
+    // call on counter (key / 4, sequence row, head, sequence).  Kept
+    // probabilities are scaled by 1 / (1 - p), dropped ones are 0.
+    auto drop4 = [&](int kt, int rb, int g4, float (&x)[4]) {
+        uint32_t c[4] = {(uint32_t)(kt * (BN / 4) + 8 * kq + hi + 2 * g4), (uint32_t)qrow(rb),
+                         (uint32_t)h, (uint32_t)b};
+        philox4x32_10(c, p.seed_lo, p.seed_hi);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = c[i] >= p.drop_threshold ? x[i] * p.drop_scale : 0.0f;
+    };
     // PV of the last tile; LO: it was a masked tile, so for bf16 its P was
     // split and the low part goes in too
     auto pv_last = [&](auto LO) {
@@ -410,7 +448,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
                     acc[rb][db] = Mma<Tin>::run(vf[db][c], p_prev[rb][c], acc[rb][db]);
-                    if constexpr (Mma<Tin>::kSplit && decltype(LO)::value)
+                    if constexpr (Mma<Tin>::kSplit && (decltype(LO)::value || DROP))
                         acc[rb][db] = Mma<Tin>::run(vf[db][c], p_lo[rb][c], acc[rb][db]);
                 }
     };
@@ -445,7 +483,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         // bf16 on a masked tile: this tile's P is split into hi + lo, and the
         // PV product of the previous tile also takes its lo part (zero when
         // that tile was not masked)
-        constexpr bool split = Mma<Tin>::kSplit && masked_tile;
+        constexpr bool split = Mma<Tin>::kSplit && (masked_tile || DROP);
         constexpr int NPV = decltype(PV)::value ? 2 * NDB * 2 : 0;
         constexpr int NPVT = split ? 2 * NPV : NPV;   // with the lo products
         constexpr int NQK = next ? 2 * NKS : 0;
@@ -519,23 +557,24 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                     pin(l[rb]);
                 }
                 if (gi >= 1) {
-                    const int u = gi - 1, rb = u >> 2, c = (u >> 1) & 1, h = u & 1;
-                    const float* x = pe[u & 1];
+                    const int u = gi - 1, rb = u >> 2, c = (u >> 1) & 1, half = u & 1;
+                    float (&x)[4] = pe[u & 1];
+                    if constexpr (DROP) drop4(j, rb, u & 3, x);
                     uint32_t a, d, alo = 0, dlo = 0;
                     pack_pair(x[0], x[1], a, alo);
                     pack_pair(x[2], x[3], d, dlo);
-                    p_new[rb][c][2 * h] = a;
-                    p_new[rb][c][2 * h + 1] = d;
+                    p_new[rb][c][2 * half] = a;
+                    p_new[rb][c][2 * half + 1] = d;
                     pin(p_new[rb][c]);
-                    if constexpr (Mma<Tin>::kNormRounded) {
+                    if constexpr (Mma<Tin>::kNormRounded && !DROP) {
                         lr[rb] = Mma<Tin>::add_pair(d, Mma<Tin>::add_pair(a, lr[rb]));
                         if constexpr (split)
                             lr[rb] = Mma<Tin>::add_pair(dlo, Mma<Tin>::add_pair(alo, lr[rb]));
                         pin(lr[rb]);
                     }
                     if constexpr (split) {
-                        p_lo_new[rb][c][2 * h] = alo;
-                        p_lo_new[rb][c][2 * h + 1] = dlo;
+                        p_lo_new[rb][c][2 * half] = alo;
+                        p_lo_new[rb][c][2 * half + 1] = dlo;
                         pin(p_lo_new[rb][c]);
                     }
                 }
@@ -597,6 +636,11 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                     }
                     psum[rb][(gi - 1) >> 1] = (pe[0] + pe[1]) + (pe[2] + pe[3]);
                     pin(psum[rb][(gi - 1) >> 1]);
+                    if constexpr (DROP) {
+                        drop4(j, rb, (gi - 1) >> 1, pe);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) s_cur[rb][e0 + i] = pe[i];
+                    }
                 } else {
                     // P^T operand of 16-key chunk c of row block rb
                     const int rb = (gi - 9) >> 1, c = (gi - 9) & 1;
@@ -795,7 +839,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             }
             // masked steps up to n_kt - 2 (the low part of P is zero for
             // the unmasked tile before the first of them)
-            if constexpr (Mma<Tin>::kSplit) clear_p_lo();
+            if constexpr (Mma<Tin>::kSplit && !kSplitAll) clear_p_lo();
             for (; j <= n_kt - 2; ++j) masked(j, SAFE);
             // last tile jl: no copy in flight, no product S(jl+1); then its own PV
             {
@@ -910,6 +954,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 #pragma unroll
             for (int db = 0; db < NDB; ++db) vf[db][c] = u32x4_t{0u, 0u, 0u, 0u};
         }
+        if constexpr (kSplitAll) clear_p_lo();
         run_keys(std::true_type(), false);
         publish();
     }
@@ -924,7 +969,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         // O is normalised by the sum of the rounded P (bf16) or the fp32 sum
         // (fp16); LSE uses the fp32 sum.
         const float lt = r.lf + partner(r.lf);
-        const float ln = Mma<Tin>::kNormRounded ? r.lrf + partner(r.lrf) : lt;
+        const float ln = Mma<Tin>::kNormRounded && !DROP ? r.lrf + partner(r.lrf) : lt;
         if (qrow(rb) < lq_b) {
             const float inv = ln > 0.0f ? 1.0f / ln : 0.0f;
             const int64_t orow = (packed ? 0 : (int64_t)b * p.o_sb) +
@@ -1054,7 +1099,7 @@ __device__ __forceinline__ bool packed_item(const FwdParams& p, int& b, int& qti
 //     items goes heaviest-first and the second half lightest-first, so that
 //     the two work-groups a CU holds (dispatched half a grid apart) sum to
 //     about the same work everywhere.
-template <int D, typename Tin, typename Tout, bool CAUSAL, bool PAIRS>
+template <int D, typename Tin, typename Tout, bool CAUSAL, bool PAIRS, bool DROP>
 __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn_fwd_mfma_kernel(
     FwdParams p, int n_qtiles, int pair) {
     // every argument the work-group reads, requested in one round trip
@@ -1082,7 +1127,7 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
         if (CAUSAL)
             t = pair == 2 ? (item < n_qtiles / 2 ? n_qtiles - 1 - item : item - n_qtiles / 2)
                           : n_qtiles - 1 - item;
-        attend_qtile<D, Tin, Tout, CAUSAL>(p, t, h, b, span);
+        attend_qtile<D, Tin, Tout, CAUSAL, DROP>(p, t, h, b, span);
     } else {
         // causal, q-tiles n-1-item and item one after the other
         int tile[2] = {n_qtiles - 1 - item, -1};
@@ -1095,12 +1140,12 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
             int hh = __builtin_amdgcn_readfirstlane(h), bb = __builtin_amdgcn_readfirstlane(b);
             asm volatile("" : "+s"(hh), "+s"(bb));
             const SeqSpan span = p.cu_q != nullptr ? packed_span(p, bb) : SeqSpan{0, p.lq, 0, p.lk};
-            attend_qtile<D, Tin, Tout, CAUSAL>(p, tile[it], hh, bb, span);
+            attend_qtile<D, Tin, Tout, CAUSAL, DROP>(p, tile[it], hh, bb, span);
         }
     }
 }
 
-template <int D, typename Tin, typename Tout>
+template <int D, typename Tin, typename Tout, bool DROP>
 hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
     const int n_qtiles = (p.lq + kBM - 1) / kBM;
     // causal q-tile order: with two resident work-groups per CU, grid
@@ -1112,27 +1157,29 @@ hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
     const int items = (p.causal && pair == 1) ? (n_qtiles + 1) / 2 : n_qtiles;
     // grid limits (y and z below 2^16) are checked by the caller
     const dim3 grid((unsigned)p.hq, (unsigned)p.batch, (unsigned)items);
-    if (p.causal && pair == 1)
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true, true>), grid,
+    // (the dropout kernels have no q-tile-pair variant: the caller asks for
+    // order 1 only through mi_attn_fwd_select, which has no dropout)
+    if (!DROP && p.causal && pair == 1)
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true, !DROP, DROP>), grid,
                            dim3(Layout<D>::THREADS), 0, stream, p, n_qtiles, pair);
     else if (p.causal)
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true, false>), grid,
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true, false, DROP>), grid,
                            dim3(Layout<D>::THREADS), 0, stream, p, n_qtiles, pair);
     else
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, false, false>), grid,
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, false, false, DROP>), grid,
                            dim3(Layout<D>::THREADS), 0, stream, p, n_qtiles, 0);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool DROP>
 hipError_t launch_d(const FwdParams& p, int in_dtype, int out_dtype,
                     hipStream_t stream) {
     if (in_dtype == 0) {
-        return out_dtype == 2 ? launch_typed<D, f16_t, float>(p, stream)
-                              : launch_typed<D, f16_t, f16_t>(p, stream);
+        return out_dtype == 2 ? launch_typed<D, f16_t, float, DROP>(p, stream)
+                              : launch_typed<D, f16_t, f16_t, DROP>(p, stream);
     }
-    return out_dtype == 2 ? launch_typed<D, bf16_t, float>(p, stream)
-                          : launch_typed<D, bf16_t, bf16_t>(p, stream);
+    return out_dtype == 2 ? launch_typed<D, bf16_t, float, DROP>(p, stream)
+                          : launch_typed<D, bf16_t, bf16_t, DROP>(p, stream);
 }
 
 }  // namespace

@@ -5,7 +5,7 @@ namespace mi_attn {
 
 hipError_t launch_mfma_d128(const FwdParams& p, int in_dtype, int out_dtype,
                           hipStream_t stream) {
-    return launch_d<128>(p, in_dtype, out_dtype, stream);
+    return launch_d<128, false>(p, in_dtype, out_dtype, stream);
 }
 
 }  // namespace mi_attn

@@ -30,6 +30,12 @@ struct FwdParams {
     int32_t causal;
     int32_t causal_pairs;            // causal q-tile order (0, 1, 2; -1 default)
     int32_t n_cu;                    // compute units of the device
+    // dropout on P (the dropout kernels only): a key is kept iff its Philox
+    // word is at least drop_threshold = floor(p * 2^32); kept probabilities
+    // are multiplied by drop_scale = 1 / (1 - p)
+    uint32_t drop_threshold;
+    float drop_scale;
+    uint32_t seed_lo, seed_hi;       // the Philox key
 };
 
 // Parameters of the decode kernel (attn_decode.hip): a few query rows per
@@ -126,6 +132,10 @@ hipError_t launch_mfma_d64(const FwdParams& p, int in_dtype, int out_dtype,
                           hipStream_t stream);
 hipError_t launch_mfma_d128(const FwdParams& p, int in_dtype, int out_dtype,
                            hipStream_t stream);
+hipError_t launch_mfma_drop_d64(const FwdParams& p, int in_dtype, int out_dtype,
+                                hipStream_t stream);
+hipError_t launch_mfma_drop_d128(const FwdParams& p, int in_dtype, int out_dtype,
+                                 hipStream_t stream);
 hipError_t launch_decode(const DecParams& p, int in_dtype, int out_dtype, int head_dim,
                          hipStream_t stream);
 hipError_t launch_rotary(const RopeParams& p, int dtype, hipStream_t stream);

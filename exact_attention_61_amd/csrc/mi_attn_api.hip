@@ -63,7 +63,9 @@ mi_attn_status_t forward(const void* q, const void* k, const void* v,
                          const int32_t* cu_seqlens_q,
                          const int32_t* cu_seqlens_k, float scale,
                          int32_t causal, struct ihipStream_t* stream,
-                         int32_t kernel, int32_t causal_order) {
+                         int32_t kernel, int32_t causal_order,
+                         double dropout_p = 0.0, uint64_t seed = 0) {
+    if (!(dropout_p >= 0.0 && dropout_p < 1.0)) return MI_ATTN_ERR_ARG;   // NaN too
     if (kernel != MI_ATTN_KERNEL_MFMA && kernel != MI_ATTN_KERNEL_SCALAR)
         return MI_ATTN_ERR_ARG;
     if (causal_order < -1 || causal_order > 2) return MI_ATTN_ERR_ARG;
@@ -149,11 +151,21 @@ mi_attn_status_t forward(const void* q, const void* k, const void* v,
     p.causal = causal;
     p.causal_pairs = causal_order;
     p.n_cu = current_device_cus();
+    // dropout: keep a key iff its Philox word >= floor(p * 2^32); kept
+    // probabilities are scaled by 1 / (1 - p)
+    const bool drop = dropout_p > 0.0;
+    p.drop_threshold = (uint32_t)std::floor(dropout_p * 4294967296.0);
+    p.drop_scale = (float)(1.0 / (1.0 - dropout_p));
+    p.seed_lo = (uint32_t)(seed & 0xffffffffu);
+    p.seed_hi = (uint32_t)(seed >> 32);
 
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t err;
     if (kernel == MI_ATTN_KERNEL_SCALAR)
         err = mi_attn::launch_simple(p, (int)in_dtype, (int)out_dtype, head_dim, st);
+    else if (drop)
+        err = head_dim == 64 ? mi_attn::launch_mfma_drop_d64(p, (int)in_dtype, (int)out_dtype, st)
+                             : mi_attn::launch_mfma_drop_d128(p, (int)in_dtype, (int)out_dtype, st);
     else if (head_dim == 64)
         err = mi_attn::launch_mfma_d64(p, (int)in_dtype, (int)out_dtype, st);
     else
@@ -446,6 +458,24 @@ mi_attn_status_t mi_attn_fwd_select(const void* q, const void* k, const void* v,
                    head_dim, q_strides, k_strides, v_strides, o_strides,
                    cu_seqlens_q, cu_seqlens_k, scale, causal, stream,
                    (int32_t)kernel, causal_order);
+}
+
+mi_attn_status_t mi_attn_fwd_dropout(const void* q, const void* k, const void* v,
+                                     void* o, float* lse, mi_attn_dtype_t in_dtype,
+                                     mi_attn_dtype_t out_dtype, int32_t batch,
+                                     int32_t hq, int32_t hkv, int32_t lq, int32_t lk,
+                                     int32_t head_dim, const mi_attn_strides_t* q_strides,
+                                     const mi_attn_strides_t* k_strides,
+                                     const mi_attn_strides_t* v_strides,
+                                     const mi_attn_strides_t* o_strides,
+                                     const int32_t* cu_seqlens_q,
+                                     const int32_t* cu_seqlens_k, float scale,
+                                     int32_t causal, double dropout_p, uint64_t seed,
+                                     struct ihipStream_t* stream) {
+    return forward(q, k, v, o, lse, in_dtype, out_dtype, batch, hq, hkv, lq, lk,
+                   head_dim, q_strides, k_strides, v_strides, o_strides,
+                   cu_seqlens_q, cu_seqlens_k, scale, causal, stream,
+                   MI_ATTN_KERNEL_MFMA, -1, dropout_p, seed);
 }
 
 mi_attn_status_t mi_attn_rotary(void* x, mi_attn_dtype_t dtype, int32_t batch,

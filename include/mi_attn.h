@@ -277,6 +277,42 @@ MI_ATTN_API int32_t mi_attn_decode_splits(int32_t batch, int32_t hq, int32_t hkv
                                           int32_t num_splits);
 
 /*
+ * mi_attn_fwd_dropout -- mi_attn_fwd with dropout on the probabilities.
+ *
+ * The "Training integration" tutorial, sections 2.1 and 8.2: the attention
+ * module takes a dropout probability for training (0.1 in its BERT-style
+ * example) and 0 for inference.  Each probability P[i, j] of the softmax is
+ * kept with probability 1 - dropout_p and then scaled by 1 / (1 - dropout_p),
+ * or set to 0; O = (P * M) V with that mask and scale.  lse is the
+ * log-sum-exp of the softmax itself (dropout acts after the normalisation).
+ *
+ * The mask: Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011) with key (seed & 0xffffffff,
+ * seed >> 32) on counter (j / 4, i, h, b) -- key j, query row i within its
+ * sequence, query head h, batch entry (packed: sequence) b; output word
+ * j % 4 keeps key j iff it is at least floor(dropout_p * 2^32).  The same
+ * (seed, b, h, i, j) always gives the same decision, whatever the layout or
+ * the launch.
+ *
+ * Every other argument, layout, ownership and error rule is that of
+ * mi_attn_fwd.  dropout_p outside [0, 1) (or NaN) returns MI_ATTN_ERR_ARG
+ * before any HIP call; dropout_p = 0 runs mi_attn_fwd.
+ */
+MI_ATTN_API mi_attn_status_t mi_attn_fwd_dropout(const void* q, const void* k, const void* v,
+                             void* o, float* lse, mi_attn_dtype_t in_dtype,
+                             mi_attn_dtype_t out_dtype, int32_t batch,
+                             int32_t hq, int32_t hkv, int32_t lq, int32_t lk,
+                             int32_t head_dim,
+                             const mi_attn_strides_t* q_strides,
+                             const mi_attn_strides_t* k_strides,
+                             const mi_attn_strides_t* v_strides,
+                             const mi_attn_strides_t* o_strides,
+                             const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k, float scale,
+                             int32_t causal, double dropout_p, uint64_t seed,
+                             struct ihipStream_t* stream);
+
+/*
  * mi_attn_rotary -- rotary position embedding of Q or K, in place.
  *
  * The "Training integration" tutorial, section 4 (4.1-4.3): the rotary

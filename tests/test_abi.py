@@ -31,7 +31,8 @@ def test_exports_every_declared_function():
     assert set(names) == {"mi_attn_fwd", "mi_attn_fwd_select", "mi_attn_decode",
                           "mi_attn_decode_noalloc", "mi_attn_decode_noalloc_max_bytes",
                           "mi_attn_decode_workspace_size", "mi_attn_decode_splits",
-                          "mi_attn_rotary", "mi_attn_status_string", "mi_attn_version",
+                          "mi_attn_rotary", "mi_attn_fwd_dropout", "mi_attn_status_string",
+                          "mi_attn_version",
                           "mi_attn_last_hip_error"}
     for n in names:
         assert hasattr(mi.lib(), n), n
@@ -157,6 +158,24 @@ def dcall(q=A, k=A * 2, v=A * 3, o=A * 4, lse=A * 5, in_dt=1, out_dt=1, b=2, hq=
 ])
 def test_decode_rejected_before_any_hip_call(kw, code):
     assert dcall(**kw) == code
+
+
+@pytest.mark.parametrize("pdrop", [-0.1, 1.0, 1.5, math.nan, math.inf])
+def test_dropout_probability_rejected_before_any_hip_call(pdrop):
+    args = (A, A * 2, A * 3, A * 4, A * 5, 0, 0, 1, 2, 1, 16, 16, 64, None, None, None, None,
+            None, None, 0.125, 0)
+    assert mi.lib().mi_attn_fwd_dropout(*args, pdrop, 1234, None) == 6
+
+
+def test_dropout_other_rejections_match_the_forward():
+    for kw, code in [(dict(q=None), 1), (dict(in_dt=2), 4), (dict(d=96), 5), (dict(causal=2), 6)]:
+        base = dict(q=A, k=A * 2, v=A * 3, o=A * 4, lse=A * 5, in_dt=0, out_dt=0, b=1, hq=2,
+                    hkv=1, lq=16, lk=16, d=64, causal=0)
+        base.update(kw)
+        args = (base["q"], base["k"], base["v"], base["o"], base["lse"], base["in_dt"],
+                base["out_dt"], base["b"], base["hq"], base["hkv"], base["lq"], base["lk"],
+                base["d"], None, None, None, None, None, None, 0.125, base["causal"])
+        assert mi.lib().mi_attn_fwd_dropout(*args, 0.1, 7, None) == code
 
 
 def rcall(x=A, dt=1, b=2, h=4, l=100, d=128, xs=None, cu=None, offs=None, off=0, rd=128,

@@ -22,6 +22,8 @@ The five named workloads follow the shapes the pages use:
 * long_8k: B=1, H=16, L=8192, d=128, non-causal, bf16 (the L=8192, d=128
            sizing table of the fusion notes, section 3).
 * long_4k: long_8k at L=4096 (a check that HBM reads scale with L).
+* bert_dropout: bert_varlen with the tutorial's attention dropout 0.1
+           (sections 2.1 and 8.2), mask seed 2024.
 * rotary_gqa: the rotary embedding (tutorial section 4, GPT-NeoX layout,
            rotary dimension = head dimension, base 10000) of the gqa_causal
            Q and K, in place.
@@ -57,6 +59,7 @@ class Workload:
     len_range: tuple = field(default=(0, 0))   # varlen: inclusive [lo, hi]
     decode: bool = False   # a few query rows against a key/value cache
     rotary: bool = False   # the rotary embedding of Q and K, in place
+    dropout: float = 0.0   # dropout probability on P (seed 2024)
 
 
 WORKLOADS = {
@@ -73,6 +76,9 @@ WORKLOADS = {
                         "bf16", "bf16", 1.0 / math.sqrt(128.0)),
     "decode_gqa": Workload("decode_gqa", 8, 32, 8, 1, 8192, 128, True,
                            "bf16", "bf16", 1.0 / math.sqrt(128.0), decode=True),
+    "bert_dropout": Workload("bert_dropout", 8, 12, 12, 1024, 1024, 64, False,
+                             "bf16", "bf16", 1.0 / 8.0, varlen=True,
+                             len_range=(256, 1024), dropout=0.1),
     "rotary_gqa": Workload("rotary_gqa", 1, 32, 8, 4096, 4096, 128, False,
                            "bf16", "bf16", 1.0, rotary=True),
     # long_8k at half the length: its HBM read bytes should halve with L
