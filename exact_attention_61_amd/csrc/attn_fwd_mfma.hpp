@@ -1099,7 +1099,11 @@ __device__ __forceinline__ bool packed_item(const FwdParams& p, int& b, int& qti
 //     items goes heaviest-first and the second half lightest-first, so that
 //     the two work-groups a CU holds (dispatched half a grid apart) sum to
 //     about the same work everywhere.
-template <int D, typename Tin, typename Tout, bool CAUSAL, bool PAIRS, bool DROP>
+// Work-group modes: one q-tile, the causal pair (n-1-t, t), or resident
+// work-groups looping over ranked q-tiles.
+enum { kModeOne = 0, kModePairs = 1, kModeResident = 2 };
+
+template <int D, typename Tin, typename Tout, bool CAUSAL, int MODE, bool DROP>
 __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn_fwd_mfma_kernel(
     FwdParams p, int n_qtiles, int pair) {
     // every argument the work-group reads, requested in one round trip
@@ -1110,7 +1114,7 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
     int h = (int)blockIdx.x;
     int b = (int)blockIdx.y;
     const int item = (int)blockIdx.z;
-    if constexpr (!PAIRS) {
+    if constexpr (MODE == kModeOne) {
         // one q-tile per work-group: a straight-line body
         int t = item;
         SeqSpan span{0, p.lq, 0, p.lk};
@@ -1128,7 +1132,7 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
             t = pair == 2 ? (item < n_qtiles / 2 ? n_qtiles - 1 - item : item - n_qtiles / 2)
                           : n_qtiles - 1 - item;
         attend_qtile<D, Tin, Tout, CAUSAL, DROP>(p, t, h, b, span);
-    } else {
+    } else if constexpr (MODE == kModePairs) {
         // causal, q-tiles n-1-item and item one after the other
         int tile[2] = {n_qtiles - 1 - item, -1};
         if (item < tile[0]) tile[1] = item;
@@ -1141,6 +1145,28 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
             asm volatile("" : "+s"(hh), "+s"(bb));
             const SeqSpan span = p.cu_q != nullptr ? packed_span(p, bb) : SeqSpan{0, p.lq, 0, p.lk};
             attend_qtile<D, Tin, Tout, CAUSAL, DROP>(p, tile[it], hh, bb, span);
+        }
+    } else {
+        // Resident work-groups (dense input, a 1-D grid of one work-group per
+        // resident slot): the B * Hq * n q-tiles are ranked heaviest first
+        // (causal: q-tile index descending, then batch and head; otherwise
+        // any order), and in round k work-group w takes rank k * G + w for
+        // even k and k * G + G - 1 - w for odd k, so the rounds' heavy and
+        // light q-tiles pair up and every work-group gets about the same
+        // key tiles in all.
+        const int G = (int)gridDim.x, w = (int)blockIdx.x;
+        const int bh = p.batch * p.hq;
+        const int n_items = bh * n_qtiles;
+        for (int k = 0; k * G < n_items; ++k) {
+            const int r = k * G + ((k & 1) ? G - 1 - w : w);
+            if (r >= n_items) break;
+            const int qi = r / bh, hb = r - qi * bh;
+            const int t = CAUSAL ? n_qtiles - 1 - qi : qi;
+            if (k > 0) __syncthreads();  // the LDS stages are reused
+            int hh = __builtin_amdgcn_readfirstlane(hb % p.hq);
+            int bb = __builtin_amdgcn_readfirstlane(hb / p.hq);
+            asm volatile("" : "+s"(hh), "+s"(bb));
+            attend_qtile<D, Tin, Tout, CAUSAL, DROP>(p, t, hh, bb, SeqSpan{0, p.lq, 0, p.lk});
         }
     }
 }
@@ -1157,16 +1183,31 @@ hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
     const int items = (p.causal && pair == 1) ? (n_qtiles + 1) / 2 : n_qtiles;
     // grid limits (y and z below 2^16) are checked by the caller
     const dim3 grid((unsigned)p.hq, (unsigned)p.batch, (unsigned)items);
+    // resident work-groups (order 3): d = 128, dense input, no dropout
+    if constexpr (D == 128 && !DROP) {
+        if (p.causal_pairs == 3 && p.cu_q == nullptr) {
+            const int64_t n_items = (int64_t)p.batch * p.hq * n_qtiles;
+            const int slots = p.n_cu * Layout<D>::WG_PER_CU;
+            const dim3 g1((unsigned)std::min<int64_t>(n_items, slots));
+            if (p.causal)
+                hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true, kModeResident, false>),
+                                   g1, dim3(Layout<D>::THREADS), 0, stream, p, n_qtiles, 0);
+            else
+                hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, false, kModeResident, false>),
+                                   g1, dim3(Layout<D>::THREADS), 0, stream, p, n_qtiles, 0);
+            return hipGetLastError();
+        }
+    }
     // (the dropout kernels have no q-tile-pair variant: the caller asks for
     // order 1 only through mi_attn_fwd_select, which has no dropout)
     if (!DROP && p.causal && pair == 1)
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true, !DROP, DROP>), grid,
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true, DROP ? kModeOne : kModePairs, DROP>), grid,
                            dim3(Layout<D>::THREADS), 0, stream, p, n_qtiles, pair);
     else if (p.causal)
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true, false, DROP>), grid,
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, true, kModeOne, DROP>), grid,
                            dim3(Layout<D>::THREADS), 0, stream, p, n_qtiles, pair);
     else
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, false, false, DROP>), grid,
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, Tin, Tout, false, kModeOne, DROP>), grid,
                            dim3(Layout<D>::THREADS), 0, stream, p, n_qtiles, 0);
     return hipGetLastError();
 }

@@ -68,7 +68,7 @@ mi_attn_status_t forward(const void* q, const void* k, const void* v,
     if (!(dropout_p >= 0.0 && dropout_p < 1.0)) return MI_ATTN_ERR_ARG;   // NaN too
     if (kernel != MI_ATTN_KERNEL_MFMA && kernel != MI_ATTN_KERNEL_SCALAR)
         return MI_ATTN_ERR_ARG;
-    if (causal_order < -1 || causal_order > 2) return MI_ATTN_ERR_ARG;
+    if (causal_order < -1 || causal_order > 3) return MI_ATTN_ERR_ARG;
     if (in_dtype != MI_ATTN_F16 && in_dtype != MI_ATTN_BF16)
         return MI_ATTN_ERR_DTYPE;
     if (out_dtype != in_dtype && out_dtype != MI_ATTN_F32)

@@ -171,7 +171,12 @@ typedef enum mi_attn_kernel {
  *                0 one query tile per work-group, heaviest first;
  *                1 query tiles t and n-1-t in one work-group;
  *                2 one query tile per work-group, the first half of the grid
- *                  heaviest first and the second half lightest first.
+ *                  heaviest first and the second half lightest first;
+ *                3 (head_dim 128, dense inputs, causal or not) resident
+ *                  work-groups, one per slot the device holds at once,
+ *                  each looping over query tiles ranked heaviest first and
+ *                  dealt in a snake order (the fusion notes, section 5.4,
+ *                  persistent kernels); other inputs take the default.
  * Other arguments, validation, ownership and errors as for mi_attn_fwd; an
  * unknown kernel or order returns MI_ATTN_ERR_ARG with nothing enqueued.
  */

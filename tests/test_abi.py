@@ -104,7 +104,7 @@ def call(q=A, k=A * 2, v=A * 3, o=A * 4, lse=A * 5, in_dt=0, out_dt=0,
     (dict(cuq=A * 6, cuk=A * 7, qs=Strides(0, 64, 0)), 3),   # packed: always
     # mi_attn_fwd_select: unknown kernel or causal order
     (dict(select=(2, -1)), 6), (dict(select=(-1, -1)), 6),
-    (dict(select=(0, 3)), 6), (dict(select=(0, -2)), 6),
+    (dict(select=(0, 4)), 6), (dict(select=(0, -2)), 6),
     (dict(select=(1, 0), in_dt=3), 4),
 ])
 def test_rejected_before_any_hip_call(kw, code):

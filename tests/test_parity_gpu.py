@@ -446,10 +446,11 @@ def test_repeat_runs_are_bit_identical():
 # of 8, Lq != Lk both ways (bottom-right alignment, rows with no key), an odd
 # q-tile count, and every causal q-tile order the kernel has
 # (mi_attn_fwd_select's causal_order: 0 heaviest first, 1 q-tiles t and
-# n-1-t in one work-group, 2 grid halves heaviest-first and lightest-first).
+# n-1-t in one work-group, 2 grid halves heaviest-first and lightest-first,
+# 3 resident work-groups looping over ranked q-tiles).
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("order", [0, 1, 2])
+@pytest.mark.parametrize("order", [0, 1, 2, 3])
 @pytest.mark.parametrize("b,h,lq,lk,d,dtype", [
     (1, 3, 1024, 1024, 64, F16),
     (2, 5, 1024, 1024, 64, BF16),
@@ -462,3 +463,16 @@ def test_repeat_runs_are_bit_identical():
 def test_causal_tile_orders(order, b, h, lq, lk, d, dtype):
     note(f"causal order {order} b{b} h{h} lq{lq} lk{lk} d{d} {dtype}")
     dense_case(b, h, h, lq, lk, d, dtype, True, causal_order=order)
+
+
+@pytest.mark.parametrize("b,hq,hkv,lq,lk,causal", [
+    (1, 32, 8, 1024, 1024, True),     # more q-tiles than resident work-groups
+    (2, 7, 7, 700, 900, False),       # rounds that do not fill the grid
+    (1, 3, 1, 129, 2000, True),       # fewer q-tiles than work-groups
+    (3, 40, 8, 1000, 1000, True),     # several snake rounds
+])
+def test_resident_workgroups(b, hq, hkv, lq, lk, causal):
+    """Order 3 at d = 128: every q-tile computed exactly once by the
+    resident work-groups, causal or not."""
+    note(f"resident b{b} hq{hq} hkv{hkv} lq{lq} lk{lk} causal {causal}")
+    dense_case(b, hq, hkv, lq, lk, 128, BF16, causal, causal_order=3)
