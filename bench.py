@@ -258,18 +258,19 @@ def _per_dispatch(path, kernel_sub):
     return out
 
 
-def read_bytes(d):
-    """HBM-side read bytes from the L2's fabric read requests by size."""
+def read_bytes(d, agg=None):
+    """HBM-side read bytes from the L2's fabric read requests by size
+    (median over the dispatches, or agg)."""
     import statistics
-    m = lambda k: statistics.median(d[k])
+    m = lambda k: (agg or statistics.median)(d[k])
     return (32 * m("TCC_EA0_RDREQ_32B_sum") + 64 * m("TCC_EA0_RDREQ_64B_sum")
             + 128 * m("TCC_EA0_RDREQ_128B_sum"))
 
 
-def write_bytes(d):
+def write_bytes(d, agg=None):
     """Write bytes: 64-byte requests and 32-byte ones (the rest)."""
     import statistics
-    m = lambda k: statistics.median(d[k])
+    m = lambda k: (agg or statistics.median)(d[k])
     w_all, w64 = m("TCC_EA0_WRREQ_sum"), m("TCC_EA0_WRREQ_64B_sum")
     return 64 * w64 + 32 * (w_all - w64)
 
@@ -316,6 +317,41 @@ def summarize_copy(dirpath):
     print("\n".join(lines))
 
 
+def summarize_bench(dirpath):
+    """Markdown table of the bench lines under DIR/<workload>/bench.json."""
+    import workloads
+    rows = []
+    for name in workloads.WORKLOADS:
+        path = os.path.join(dirpath, name, "bench.json")
+        if not os.path.exists(path):
+            continue
+        rec = json.loads([x for x in open(path).read().splitlines() if x.startswith("{")][-1])
+        roof, base, par = rec["roofline"], rec.get("cpu_baseline") or {}, rec.get("parity") or {}
+        err = (f"{par.get('max_abs_err_o', par.get('max_abs_err', float('nan'))):.3e}"
+               if par else "-")
+        errl = f"{par['max_abs_err_lse']:.3e}" if "max_abs_err_lse" in par else "-"
+        rows.append(
+            f"| {name} | {rec['ms_per_step'] * 1e3:.2f} | {rec['value']} {rec['unit']} | "
+            f"{100 * roof['frac']:.2f} % of {roof['peak']} ({roof['bound']}) | {err} | {errl} | "
+            f"{'pass' if par.get('pass') else 'FAIL' if par else '-'} | "
+            f"{base.get('value', '-')} {base.get('unit', '')} ({base.get('cores', '-')} cores) |")
+    lines = [
+        "# Bench lines of every workload (one session, one box)", "",
+        "Command per workload (repository root, MI355X):", "",
+        "    python bench.py --workload <name>          # 200 timed steps, 20 warm-up",
+        "    python bench.py --summarize-bench DIR      # this table", "",
+        "Time per step: HIP events around graph-replayed launches on the launch stream (median "
+        "of 5 batches reported in each line's ms_per_step_median_batch).  Parity: max-abs error "
+        "of the run's GPU output against the fp64 oracle.  CPU: the oracle on the box's host "
+        "cores over whole passes of the workload (about 10 s).", "",
+        "| workload | us / step | value | roofline | max abs err O | max abs err LSE | parity "
+        "| oracle on CPU |",
+        "|---|---|---|---|---|---|---|---|",
+        *rows,
+    ]
+    print("\n".join(lines))
+
+
 def summarize_counters(dirpath, name, write_record):
     """Markdown summary of the rocprofv3 runs of one workload (see the
     commands it prints) and, optionally, the committed counter record."""
@@ -339,16 +375,20 @@ def summarize_counters(dirpath, name, write_record):
     tr = [r for r in _csv_rows(_find(os.path.join(dirpath, "trace"), "kernel_trace.csv"))
           if kern in r["Kernel_Name"]]
     dur = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr]
-    t_avg = statistics.mean(dur) * 1e-9
+    t_avg = statistics.mean(dur) * 1e-9 * (2 if w.rotary else 1)   # per step
     rd = _per_dispatch(_find(os.path.join(dirpath, "read"), "counter_collection.csv"), kern)
     wr = _per_dispatch(_find(os.path.join(dirpath, "write"), "counter_collection.csv"), kern)
     mf = _per_dispatch(_find(os.path.join(dirpath, "mfma"), "counter_collection.csv"), kern)
-    m = lambda d, k: statistics.median(d[k])
+    # a rotary step is two launches (Q, then K): figures per step are the
+    # mean over the dispatches times two; otherwise medians per dispatch
+    launches = 2 if w.rotary else 1
+    agg = (lambda xs: launches * statistics.mean(xs)) if w.rotary else statistics.median
+    m = lambda d, k: agg(d[k])
     n32, n64, n128 = (m(rd, f"TCC_EA0_RDREQ_{x}B_sum") for x in (32, 64, 128))
     nall = m(rd, "TCC_EA0_RDREQ_sum")
-    read_b = read_bytes(rd)
+    read_b = read_bytes(rd, agg)
     w_all, w64 = m(wr, "TCC_EA0_WRREQ_sum"), m(wr, "TCC_EA0_WRREQ_64B_sum")
-    write_b = write_bytes(wr)
+    write_b = write_bytes(wr, agg)
     busy = m(mf, "SQ_VALU_MFMA_BUSY_CYCLES")
     # GRBM_GUI_ACTIVE adds up the 8 XCDs' active cycles; it also counts
     # the profiler's window around a short dispatch, so it is context only
@@ -360,6 +400,8 @@ def summarize_counters(dirpath, name, write_record):
     h = kernel_hash()
     q, k, v = inp["q"], inp["k"], inp["v"]
     in_b = (q.numel() + k.numel() + v.numel()) * 2
+    if w.rotary:                         # Q and K in, Q and K out
+        in_b = (q.numel() + k.numel()) * 2
     lines = [
         f"# {kern} — {name} — kernel trace, HBM bytes and MFMA counters", "",
         f"Workload: {metric_label(w)}; {flops / 1e9:.3f} GFLOP algorithmic per launch, "
@@ -370,7 +412,8 @@ def summarize_counters(dirpath, name, write_record):
         f"    python bench.py --summarize-counters DIR --workload {name}", "",
         "Counter figures are medians over the kernel's dispatches in each run.", "",
         "| quantity | per launch |", "|---|---|",
-        f"| kernel duration (trace, {len(dur)} dispatches) | mean {t_avg * 1e6:.2f} us, median "
+        f"| kernel duration (trace, {len(dur)} dispatches{', two per step' if w.rotary else ''}) "
+        f"| mean {t_avg * 1e6:.2f} us per step, median dispatch "
         f"{statistics.median(dur) / 1e3:.2f} us, min {min(dur) / 1e3:.2f} us |",
         f"| algorithmic TFLOP/s at the mean duration | {flops / t_avg / 1e12:.1f} "
         f"({100 * flops / t_avg / 1e12 / PEAK_TFLOPS[w.in_dtype]:.2f} % of {PEAK_TFLOPS[w.in_dtype]}) |",
@@ -378,16 +421,18 @@ def summarize_counters(dirpath, name, write_record):
         f"({100 * nbytes / t_avg / 1e9 / PEAK_HBM_GBS:.1f} % of {PEAK_HBM_GBS:.0f}) |",
         f"| read requests 32 B / 64 B / 128 B (all) | {n32:.0f} / {n64:.0f} / {n128:.0f} ({nall:.0f}) |",
         f"| HBM read bytes (32·n32 + 64·n64 + 128·n128) | {read_b / 2**20:.2f} MiB = "
-        f"{read_b / in_b:.3f} x Q+K+V ({in_b / 2**20:.2f} MiB) |",
+        f"{read_b / in_b:.3f} x {'Q+K' if w.rotary else 'Q+K+V'} ({in_b / 2**20:.2f} MiB) |",
         f"| write requests (64 B of them) | {w_all:.0f} ({w64:.0f}) |",
-        f"| HBM write bytes | {write_b / 2**20:.2f} MiB = {write_b / (nbytes - in_b):.3f} x O+LSE "
-        f"({(nbytes - in_b) / 2**20:.2f} MiB) |",
+        (f"| HBM write bytes | {write_b / 2**20:.2f} MiB = {write_b / in_b:.3f} x Q+K "
+         f"({in_b / 2**20:.2f} MiB) |" if w.rotary else
+         f"| HBM write bytes | {write_b / 2**20:.2f} MiB = {write_b / (nbytes - in_b):.3f} x O+LSE "
+         f"({(nbytes - in_b) / 2**20:.2f} MiB) |"),
         f"| MFMA busy: busy cycles / ({SIMDS} SIMDs x 2.4 GHz x mean duration) | "
         f"{100 * busy_peak:.1f} % |",
         f"| MFMA busy against GRBM_GUI_ACTIVE / 8 (context: includes the profiler's "
         f"window) | {100 * busy_gui:.1f} % |",
-        f"| executed MFMA flops (MOPS x 512) | {exec_flops / 1e9:.3f} GFLOP = "
-        f"{exec_flops / flops:.3f} x algorithmic |", "",
+        f"| executed MFMA flops (MOPS x 512) | {exec_flops / 1e9:.3f} GFLOP"
+        + (f" = {exec_flops / flops:.3f} x algorithmic |" if flops else " |"), "",
         f"Kernel source sha256[:16] = {h}.",
     ]
     print("\n".join(lines))
@@ -425,6 +470,8 @@ def main():
     ap.add_argument("--summarize-counters", default=None, metavar="DIR",
                     help="print the Markdown summary of the rocprofv3 runs "
                          "under DIR (no GPU work)")
+    ap.add_argument("--summarize-bench", default=None, metavar="DIR",
+                    help="print the Markdown table of the bench lines under DIR (no GPU work)")
     ap.add_argument("--summarize-copy", default=None, metavar="DIR",
                     help="print the Markdown summary of the copy calibration's "
                          "counter runs under DIR (no GPU work)")
@@ -443,6 +490,9 @@ def main():
         sys.exit(2)
     if args.summarize_copy:
         summarize_copy(args.summarize_copy)
+        return
+    if args.summarize_bench:
+        summarize_bench(args.summarize_bench)
         return
     if args.summarize_counters:
         import workloads
