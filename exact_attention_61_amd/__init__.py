@@ -261,8 +261,8 @@ def mi_attn_decode(q, k, v, o, lse=None, *, seqlens_k=None, causal=True, scale=N
     q, o: [B, Hq, Lq, d] (Lq <= 32); k, v: the cache [B, Hkv, Lk, d]; lse
     [B, Hq, Lq] float32 or None; seqlens_k: int32 [B] keys per sequence or
     None (all Lk).  workspace: a uint8 tensor of at least
-    mi_attn_decode_workspace_size(...) bytes whose counters start at zero
-    (torch.zeros), or None when that size is 0.
+    mi_attn_decode_workspace_size(...) bytes (any contents), or None when
+    that size is 0.
     """
     _decode_call(q, k, v, o, lse, seqlens_k, causal, scale, num_splits, workspace, stream,
                  noalloc=False)
@@ -307,7 +307,7 @@ def _decode_call(q, k, v, o, lse, seqlens_k, causal, scale, num_splits, workspac
 
 def decode(q, k, v, *, seqlens_k=None, causal=True, scale=None, num_splits=0,
            out_dtype=None, workspace=None, return_lse=True):
-    """Allocate out (and lse, and a zeroed workspace unless given) and run
+    """Allocate out (and lse, and a workspace unless given) and run
     mi_attn_decode; returns (out, lse)."""
     out_dtype = q.dtype if out_dtype is None else out_dtype
     out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
@@ -317,7 +317,7 @@ def decode(q, k, v, *, seqlens_k=None, causal=True, scale=None, num_splits=0,
     if workspace is None:
         n = mi_attn_decode_workspace_size(bsz, hq, hkv, lq, lk, q.shape[-1], num_splits)
         if n > 0:
-            workspace = torch.zeros(n, dtype=torch.uint8, device=q.device)
+            workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
     with torch.cuda.device(q.device):
         mi_attn_decode(q, k, v, out, lse, seqlens_k=seqlens_k, causal=causal, scale=scale,
                        num_splits=num_splits, workspace=workspace)

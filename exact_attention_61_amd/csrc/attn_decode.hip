@@ -24,9 +24,11 @@
 //
 // After the key loop the 4 waves merge through LDS.  With one split the
 // work-group writes O and LSE; otherwise it writes its normalised partial
-// output and (m, l) per row to the workspace, and the last split of the
-// query group to arrive (an atomic counter per query group, reset to zero by
-// that work-group) merges all partials and writes O and LSE.
+// output and (m, l) per row to the workspace, and a second kernel on the same
+// stream merges the splits of every row and writes O and LSE.  (Merging in
+// the last split to arrive needs a device-scope release and acquire around an
+// arrival counter; with eight L2s those fences and the atomic cost ~30 us per
+// launch, more than the whole merge kernel.)
 #include <type_traits>
 
 #include "../../include/mi_attn.h"
@@ -326,60 +328,57 @@ __global__ __launch_bounds__(kDecThreads, 1) void attn_decode_kernel(DecParams p
         pm[0] = M;                       // log2 domain, -inf for a row with no key here
         pm[1] = Lsum;
     }
+}
 
-    // ---- the last split of the query group merges ---------------------------
-    __shared__ int last_flag;
-    __threadfence();                     // this split's partials are visible
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t* cnt = p.counters + ((int64_t)b * p.hkv + g) * p.nqg + qg;
-        const int old = atomicAdd(cnt, 1);
-        const int last = old == p.splits - 1;
-        if (last) atomicExch(cnt, 0);    // ready for the next call
-        last_flag = last;
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();                     // the other splits' partials are visible
-    // thread t: row t / 8 of the group, columns (t % 8) * D/8 .. +D/8-1
-    const int r = (int)threadIdx.x >> 3;
-    if (r >= rows) return;
-    const int hr = r / p.lq, pr = r - (r / p.lq) * p.lq;
-    const int64_t rid = ((int64_t)b * p.hq + h0 + hr) * p.lq + pr;
+// Merge of the splits of one row per wave: m = max of the parts, each part's
+// exp-sum and normalised output weighted by l_s 2^(m_s - m) (the combination
+// rule of the online softmax, as across work-groups).  Lane j holds columns
+// j, j + 64, ... of the row.
+constexpr int kCombineRows = 4;          // rows (waves) per work-group
+
+template <int D, typename Tout>
+__global__ __launch_bounds__(64 * kCombineRows) void attn_decode_combine_kernel(DecParams p) {
+    constexpr int CPL = D / 64;          // columns per lane
+    const int64_t rows = (int64_t)p.batch * p.hq * p.lq;
+    const int64_t rid = (int64_t)blockIdx.x * kCombineRows + (threadIdx.x >> 6);
+    if (rid >= rows) return;
+    const int lane = (int)threadIdx.x & 63;
+    const int pos = (int)(rid % p.lq);
+    const int64_t bh = rid / p.lq;
+    const int hq = (int)(bh % p.hq), b = (int)(bh / p.hq);
     const float* pm = p.part_ml + rid * p.splits * 2;
-    float Mx = -__builtin_inff();
-    for (int s = 0; s < p.splits; ++s) Mx = max2(Mx, pm[2 * s]);
-    const float mux = Mx == -__builtin_inff() ? 0.0f : Mx;
-    float Lx = 0.0f;
-    for (int s = 0; s < p.splits; ++s) Lx += pm[2 * s + 1] * fast_exp2(pm[2 * s] - mux);
-    const float invx = Lx > 0.0f ? 1.0f / Lx : 0.0f;
-    constexpr int CPTH = D / 8;          // columns per thread
-    float ox[CPTH];
+    const float* po = p.part_o + rid * p.splits * D + lane;
+    float M = -__builtin_inff();
+    for (int s = 0; s < p.splits; ++s) M = max2(M, pm[2 * s]);
+    const float mu = M == -__builtin_inff() ? 0.0f : M;
+    float L = 0.0f;
+    float o[CPL];
 #pragma unroll
-    for (int c = 0; c < CPTH; ++c) ox[c] = 0.0f;
-    const int c0 = ((int)threadIdx.x & 7) * CPTH;
+    for (int c = 0; c < CPL; ++c) o[c] = 0.0f;
     for (int s = 0; s < p.splits; ++s) {
-        const float w = pm[2 * s + 1] * fast_exp2(pm[2 * s] - mux) * invx;
-        const float* po = p.part_o + (rid * p.splits + s) * D + c0;
+        const float w = pm[2 * s + 1] * fast_exp2(pm[2 * s] - mu);
+        L += w;
 #pragma unroll
-        for (int c = 0; c < CPTH; c += 4) {
-            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(po + c);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ox[c + i] = fmaf(x[i], w, ox[c + i]);
-        }
+        for (int c = 0; c < CPL; ++c) o[c] = fmaf(po[s * D + 64 * c], w, o[c]);
     }
-    const int64_t orow = (int64_t)b * p.o_sb + (int64_t)(h0 + hr) * p.o_sh + (int64_t)pr * p.o_sr;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const int64_t orow = (int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + (int64_t)pos * p.o_sr;
 #pragma unroll
-    for (int c = 0; c < CPTH; c += 4)
-        Epi<Tout>::store4(p.o, orow + c0 + c, ox[c], ox[c + 1], ox[c + 2], ox[c + 3]);
-    if ((threadIdx.x & 7) == 0 && p.lse != nullptr)
-        p.lse[rid] = Lx > 0.0f ? (mux + __log2f(Lx)) * 0.69314718055994530942f : -__builtin_inff();
+    for (int c = 0; c < CPL; ++c) OutStore<Tout>::put(p.o, orow + lane + 64 * c, o[c] * inv);
+    if (lane == 0 && p.lse != nullptr)
+        p.lse[rid] = L > 0.0f ? (mu + __log2f(L)) * 0.69314718055994530942f : -__builtin_inff();
 }
 
 template <int D, typename Tin, typename Tout>
 hipError_t launch_decode_typed(const DecParams& p, hipStream_t stream) {
     const dim3 grid((unsigned)p.splits, (unsigned)(p.hkv * p.nqg), (unsigned)p.batch);
     hipLaunchKernelGGL((attn_decode_kernel<D, Tin, Tout>), grid, dim3(kDecThreads), 0, stream, p);
+    if (p.splits > 1) {
+        const int64_t rows = (int64_t)p.batch * p.hq * p.lq;
+        const dim3 g2((unsigned)((rows + kCombineRows - 1) / kCombineRows));
+        hipLaunchKernelGGL((attn_decode_combine_kernel<D, Tout>), g2, dim3(64 * kCombineRows), 0,
+                           stream, p);
+    }
     return hipGetLastError();
 }
 

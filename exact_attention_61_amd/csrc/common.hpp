@@ -63,7 +63,6 @@ struct DecParams {
     int32_t causal;                  // bottom-right: j <= i + Lk_b - Lq
     float* part_o;                   // [B, Hq, Lq, splits, d] partial outputs
     float* part_ml;                  // [B, Hq, Lq, splits, 2] (m in log2, l)
-    int32_t* counters;               // [B, hkv, nqg] arrivals, zero between calls
 };
 
 // Parameters of the rotary-embedding kernel (rotary.hip).  x is rotated in

@@ -188,7 +188,7 @@ constexpr int kCUs = 256;                // MI355X compute units
 
 struct DecodePlan {
     int32_t hpg, nqg, splits, chunk;
-    size_t off_ml, off_cnt, bytes;       // workspace layout (bytes == 0: none)
+    size_t off_ml, bytes;                // workspace layout (bytes == 0: none)
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -218,30 +218,22 @@ DecodePlan decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t lq, int32
     if (pl.splits == 1) return pl;
     const size_t rows = (size_t)batch * hq * lq * pl.splits;
     pl.off_ml = align256(rows * head_dim * 4);
-    pl.off_cnt = pl.off_ml + align256(rows * 2 * 4);
-    pl.bytes = pl.off_cnt + align256((size_t)groups * 4);
+    pl.bytes = pl.off_ml + align256(rows * 2 * 4);
     return pl;
 }
 
 // ---------------------------------------------------------------------------
 // Static scratch of mi_attn_decode_noalloc: a file-scope device array, one
 // copy per GPU, reached through the address hipGetSymbolAddress gives on that
-// device (the array's name is only a host-side stand-in).  The first 64 KiB
-// are the arrival counters (one per query group, at most 16384 groups);
-// the partial results follow.  The counters are cleared once per device at
-// set-up and every call leaves them at zero.
+// device (the array's name is only a host-side stand-in).  It holds the
+// partial results of one call (the workspace layout); nothing in it has to
+// start at any value.
 // ---------------------------------------------------------------------------
 
 constexpr size_t kScratchBytes = size_t(8) << 20;           // 8 MiB per GPU
-constexpr size_t kScratchCounterBytes = size_t(64) << 10;   // 16384 counters
 constexpr int kMaxDevices = 64;
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
-
-__global__ void clear_words_kernel(int32_t* w, int n) {
-    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
-    if (i < n) w[i] = 0;
-}
 
 struct ScratchSlot {
     std::once_flag once;
@@ -250,9 +242,9 @@ struct ScratchSlot {
 };
 ScratchSlot g_scratch[kMaxDevices];
 
-// The scratch address on the current device; on the first call for the
-// device its counter region is cleared by a fill kernel on `stream`.
-hipError_t scratch_on_current_device(hipStream_t stream, char** out) {
+// The scratch address on the current device, looked up on the first call
+// for the device.
+hipError_t scratch_on_current_device(char** out) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -261,26 +253,16 @@ hipError_t scratch_on_current_device(hipStream_t stream, char** out) {
     std::call_once(slot.once, [&]() {
         void* ptr = nullptr;
         slot.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
-        if (slot.err != hipSuccess) return;
-        const int n = (int)(kScratchCounterBytes / 4);
-        hipLaunchKernelGGL(clear_words_kernel, dim3((n + 255) / 256), dim3(256), 0, stream,
-                           static_cast<int32_t*>(ptr), n);
-        slot.err = hipGetLastError();
         if (slot.err == hipSuccess) slot.ptr = static_cast<char*>(ptr);
     });
     *out = slot.ptr;
     return slot.err;
 }
 
-bool fits_scratch(const DecodePlan& pl, int32_t batch, int32_t hkv) {
-    const int64_t groups = (int64_t)batch * hkv * pl.nqg;
-    return groups * 4 <= (int64_t)kScratchCounterBytes &&
-           pl.off_cnt <= kScratchBytes - kScratchCounterBytes;
-}
+bool fits_scratch(const DecodePlan& pl) { return pl.bytes <= kScratchBytes; }
 
 // Validation and launch of the decode path.  `workspace` (bytes) holds the
-// partial results and the arrival counters; the counters must be zero
-// before the first call and are zero again after every call.
+// partial results of the splits (no state is kept between calls).
 mi_attn_status_t decode(const void* q, const void* k, const void* v, void* o, float* lse,
                         mi_attn_dtype_t in_dtype, mi_attn_dtype_t out_dtype, int32_t batch,
                         int32_t hq, int32_t hkv, int32_t lq, int32_t lk, int32_t head_dim,
@@ -318,7 +300,7 @@ mi_attn_status_t decode(const void* q, const void* k, const void* v, void* o, fl
     const DecodePlan pl = decode_plan(batch, hq, hkv, lq, lk, head_dim, num_splits);
     if ((int64_t)hkv * pl.nqg > 65535) return MI_ATTN_ERR_SHAPE;
     if (use_scratch) {
-        if (pl.bytes > 0 && !fits_scratch(pl, batch, hkv)) return MI_ATTN_ERR_WORKSPACE;
+        if (pl.bytes > 0 && !fits_scratch(pl)) return MI_ATTN_ERR_WORKSPACE;
     } else if (pl.bytes > 0) {
         if (workspace == nullptr) return MI_ATTN_ERR_NULL;
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MI_ATTN_ERR_LAYOUT;
@@ -327,8 +309,7 @@ mi_attn_status_t decode(const void* q, const void* k, const void* v, void* o, fl
     // the static scratch of this device (set up on the first call)
     char* scratch_base = nullptr;
     if (use_scratch && pl.bytes > 0) {
-        const hipError_t e = scratch_on_current_device(
-            reinterpret_cast<hipStream_t>(stream), &scratch_base);
+        const hipError_t e = scratch_on_current_device(&scratch_base);
         if (e != hipSuccess) {
             g_last_hip_error = (int32_t)e;
             return MI_ATTN_ERR_HIP;
@@ -351,16 +332,10 @@ mi_attn_status_t decode(const void* q, const void* k, const void* v, void* o, fl
     p.scale_log2 = (float)std::fmax(std::fabs((double)scale) * 1.4426950408889634074, 1e-30);
     p.negate_q = scale < 0.0f ? 1 : 0;
     p.causal = causal;
-    if (pl.bytes > 0 && use_scratch) {
-        // counters in the fixed region at the front, the partials after it
-        p.counters = reinterpret_cast<int32_t*>(scratch_base);
-        p.part_o = reinterpret_cast<float*>(scratch_base + kScratchCounterBytes);
-        p.part_ml = reinterpret_cast<float*>(scratch_base + kScratchCounterBytes + pl.off_ml);
-    } else if (pl.bytes > 0) {
-        char* ws = static_cast<char*>(workspace);
+    if (pl.bytes > 0) {
+        char* ws = use_scratch ? scratch_base : static_cast<char*>(workspace);
         p.part_o = reinterpret_cast<float*>(ws);
         p.part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
-        p.counters = reinterpret_cast<int32_t*>(ws + pl.off_cnt);
     }
     const hipError_t err = mi_attn::launch_decode(p, (int)in_dtype, (int)out_dtype, head_dim,
                                                   reinterpret_cast<hipStream_t>(stream));
@@ -406,7 +381,7 @@ mi_attn_status_t mi_attn_decode_noalloc(const void* q, const void* k, const void
                   num_splits, nullptr, 0, stream, true);
 }
 
-size_t mi_attn_decode_noalloc_max_bytes(void) { return kScratchBytes - kScratchCounterBytes; }
+size_t mi_attn_decode_noalloc_max_bytes(void) { return kScratchBytes; }
 
 mi_attn_status_t mi_attn_decode(const void* q, const void* k, const void* v, void* o,
                                 float* lse, mi_attn_dtype_t in_dtype,

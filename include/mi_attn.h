@@ -219,10 +219,10 @@ MI_ATTN_API mi_attn_status_t mi_attn_fwd_select(const void* q, const void* k, co
  * workspace, workspace_bytes  device memory of at least
  *           mi_attn_decode_workspace_size(...) bytes, 256-byte aligned, or
  *           NULL when that size is 0 (a single split).  It holds the partial
- *           results and one arrival counter per query group; the counters
- *           must be zero before the first call (e.g. a zero-filled buffer)
- *           and every call leaves them at zero.  Calls that share one
- *           workspace must not overlap in time.
+ *           results of the splits, which a second kernel on the same stream
+ *           merges; its contents need no initial value and nothing is kept
+ *           between calls.  Calls that share one workspace must not overlap
+ *           in time.
  * Other arguments, ownership, validation and errors as for mi_attn_fwd;
  * Lq above 32 returns MI_ATTN_ERR_SHAPE, a NULL or short workspace
  * MI_ATTN_ERR_NULL / MI_ATTN_ERR_WORKSPACE, a workspace not 256-byte
@@ -245,16 +245,14 @@ MI_ATTN_API mi_attn_status_t mi_attn_decode(const void* q, const void* k, const 
 /*
  * mi_attn_decode_noalloc — mi_attn_decode for callers that cannot allocate
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc): the partial results and arrival counters live in a static
- * device array of the library, 8 MiB per GPU, held until the process ends.
- * It calls no hipMalloc, hipFree or other allocating routine.
+ * hipMalloc): the partial results live in a static device array of the
+ * library, 8 MiB per GPU, held until the process ends.  It calls no
+ * hipMalloc, hipFree or other allocating routine.
  *
  * Sizes whose partial results need more than
- * mi_attn_decode_noalloc_max_bytes() (8 MiB minus the 64 KiB counter
- * region), or more than 16384 query groups (batch * hkv * query groups per
- * kv head), return MI_ATTN_ERR_WORKSPACE before any HIP call.  The first
- * call on a device clears the counters with a small kernel on its stream;
- * every call leaves them at zero.  All calls on one GPU share the array:
+ * mi_attn_decode_noalloc_max_bytes() (8 MiB) return MI_ATTN_ERR_WORKSPACE
+ * before any HIP call.  The array needs no initial value.  All calls on one
+ * GPU share the array:
  * calls that overlap in time on one GPU (other streams, other threads)
  * race and give wrong results.  Arguments otherwise as for mi_attn_decode.
  */

@@ -127,9 +127,10 @@ def test_decode_worked_example(dtype):
     assert abs(lse[0, 0, 0] - math.log(3.0)) <= 1e-6
 
 
-def test_decode_counters_reset_and_reuse():
-    """Every call leaves the workspace's arrival counters at zero, so one
-    workspace serves call after call."""
+def test_decode_workspace_reuse():
+    """One workspace serves call after call, whatever it held before: the
+    results of three calls on a workspace filled with garbage are identical
+    and match the oracle."""
     import exact_attention_61_amd as mi
     note("decode workspace reuse")
     dev = torch.device("cuda", 0)
@@ -137,22 +138,17 @@ def test_decode_counters_reset_and_reuse():
     q, k, v = workloads.make_dense(b, hq, hkv, lq, lk, d, BF16, seed=6)
     qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
     n = mi.mi_attn_decode_workspace_size(b, hq, hkv, lq, lk, d, req)
-    splits = mi.mi_attn_decode_splits(b, hq, hkv, lq, lk, d, req)
-    assert splits == req and n > 0
-    ws = torch.zeros(n, dtype=torch.uint8, device=dev)
+    assert mi.mi_attn_decode_splits(b, hq, hkv, lq, lk, d, req) == req and n > 0
+    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device=dev)
     o_ref, l_ref = oracle_decode(q, k, v, None, None, True)
-    # layout: partial outputs, partial (m, l), then one counter per query
-    # group (8 / 2 = 4 heads x 2 rows fit one group of 32 rows)
-    align = lambda x: (x + 255) // 256 * 256
-    rows = b * hq * lq * splits
-    off_cnt = align(rows * d * 4) + align(rows * 2 * 4)
-    groups = b * hkv * 1
+    outs = []
     for _ in range(3):
         o, lse = mi.decode(qg, kg, vg, num_splits=req, workspace=ws)
         torch.cuda.synchronize()
-        compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, l_ref)
-        cnt = ws[off_cnt:off_cnt + 4 * groups].view(torch.int32)
-        assert torch.count_nonzero(cnt).item() == 0
+        outs.append((o.double().cpu().numpy(), lse.double().cpu().numpy()))
+        compare(outs[-1][0], outs[-1][1], o_ref, l_ref)
+    for o, lse in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(lse, outs[0][1])
 
 
 @pytest.mark.parametrize("name", ["decode_gqa"])
