@@ -1118,6 +1118,13 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
         // one q-tile per work-group: a straight-line body
         int t = item;
         SeqSpan span{0, p.lq, 0, p.lk};
+        // Grouped heads: the dispatcher deals consecutive work-groups to the
+        // 8 XCDs in turn, so with hq a multiple of 8 the work-group of grid
+        // column x runs on XCD x % 8.  Taking head (x % 8) * (hq / 8) + x / 8
+        // puts hq / 8 consecutive heads -- whole kv groups when the group
+        // size divides hq / 8 -- on one XCD, where they share its L2 for K
+        // and V.
+        if (p.hq > p.hkv && (p.hq & 7) == 0) h = (h & 7) * (p.hq >> 3) + (h >> 3);
         if (p.cu_q != nullptr) {
             if (!CAUSAL && p.batch <= 64) {
                 if (!packed_item<Layout<D>::WG_PER_CU>(p, b, t, h, span)) return;
