@@ -1110,7 +1110,7 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
     asm volatile("" ::"s"(p.q), "s"(p.k), "s"(p.v), "s"(p.o), "s"(p.lse),
                  "s"(p.q_sh), "s"(p.k_sh), "s"(p.v_sh), "s"(p.q_sr), "s"(p.k_sr),
                  "s"(p.v_sr), "s"(p.o_sh), "s"(p.o_sr), "s"(p.lq), "s"(p.lk),
-                 "s"(p.group_magic), "s"(p.scale_log2));
+                 "s"(p.group_magic), "s"(p.scale_log2), "s"(n_qtiles), "s"(pair));
     int h = (int)blockIdx.x;
     int b = (int)blockIdx.y;
     const int item = (int)blockIdx.z;
