@@ -375,14 +375,11 @@ def summarize_counters(dirpath, name, write_record):
     tr = [r for r in _csv_rows(_find(os.path.join(dirpath, "trace"), "kernel_trace.csv"))
           if kern in r["Kernel_Name"]]
     dur = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr]
-    t_avg = statistics.mean(dur) * 1e-9 * (2 if w.rotary else 1)   # per step
+    t_avg = statistics.mean(dur) * 1e-9  # per launch (one per step)
     rd = _per_dispatch(_find(os.path.join(dirpath, "read"), "counter_collection.csv"), kern)
     wr = _per_dispatch(_find(os.path.join(dirpath, "write"), "counter_collection.csv"), kern)
     mf = _per_dispatch(_find(os.path.join(dirpath, "mfma"), "counter_collection.csv"), kern)
-    # a rotary step is two launches (Q, then K): figures per step are the
-    # mean over the dispatches times two; otherwise medians per dispatch
-    launches = 2 if w.rotary else 1
-    agg = (lambda xs: launches * statistics.mean(xs)) if w.rotary else statistics.median
+    agg = statistics.median              # counters: medians per dispatch
     m = lambda d, k: agg(d[k])
     n32, n64, n128 = (m(rd, f"TCC_EA0_RDREQ_{x}B_sum") for x in (32, 64, 128))
     nall = m(rd, "TCC_EA0_RDREQ_sum")
@@ -405,15 +402,15 @@ def summarize_counters(dirpath, name, write_record):
     lines = [
         f"# {kern} — {name} — kernel trace, HBM bytes and MFMA counters", "",
         f"Workload: {metric_label(w)}; {flops / 1e9:.3f} GFLOP algorithmic per launch, "
-        f"{nbytes} algorithmic bytes (Q+K+V read once, O+LSE written once).", "",
+        f"{nbytes} algorithmic bytes " + ("(Q and K read and written once)." if w.rotary else "(Q+K+V read once, O+LSE written once)."), "",
         "Commands (repository root, MI355X, `TMPDIR=/tmp`, library built by "
         "`python exact_attention_61_amd/build.py`; each counter pass its own run):", "",
         *[f"    {c}" for c in cmds.values()],
         f"    python bench.py --summarize-counters DIR --workload {name}", "",
         "Counter figures are medians over the kernel's dispatches in each run.", "",
         "| quantity | per launch |", "|---|---|",
-        f"| kernel duration (trace, {len(dur)} dispatches{', two per step' if w.rotary else ''}) "
-        f"| mean {t_avg * 1e6:.2f} us per step, median dispatch "
+        f"| kernel duration (trace, {len(dur)} dispatches) "
+        f"| mean {t_avg * 1e6:.2f} us, median dispatch "
         f"{statistics.median(dur) / 1e3:.2f} us, min {min(dur) / 1e3:.2f} us |",
         f"| algorithmic TFLOP/s at the mean duration | {flops / t_avg / 1e12:.1f} "
         f"({100 * flops / t_avg / 1e12 / PEAK_TFLOPS[w.in_dtype]:.2f} % of {PEAK_TFLOPS[w.in_dtype]}) |",
@@ -548,15 +545,13 @@ def main():
         # one rotation of fresh copies for the parity check, then the timed
         # steps rotate q and k in place again and again
         qr, kr = q.clone(), k.clone()
-        mi.mi_attn_rotary(qr, w.d)
-        mi.mi_attn_rotary(kr, w.d)
+        mi.mi_attn_rotary_qk(qr, kr, w.d)
         torch.cuda.synchronize()
         rotated = [x.to("cpu", torch.float64).numpy() for x in (qr, kr)]
         del qr, kr
 
         def step():
-            mi.mi_attn_rotary(q, w.d)
-            mi.mi_attn_rotary(k, w.d)
+            mi.mi_attn_rotary_qk(q, k, w.d)
     elif w.dropout:
         def step():
             mi.mi_attn_fwd_dropout(q, k, v, o, lse, dropout_p=w.dropout, seed=DROPOUT_SEED,

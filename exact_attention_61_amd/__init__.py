@@ -14,6 +14,9 @@ Entry points mirror the C ABI of include/mi_attn.h:
 * mi_attn_decode_noalloc(q, k, v, o, lse, ...) -- the same with its scratch
   in a static device array of the library (no allocation at all);
 * mi_attn_decode_workspace_size(...), mi_attn_decode_splits(...);
+* mi_attn_fwd_dropout(..., dropout_p=, seed=) -- dropout on the probabilities;
+* mi_attn_rotary(x, ...), mi_attn_rotary_qk(q, k, ...) -- rotary position
+  embedding in place (one tensor, or Q and K in one launch);
 * mi_attn_status_string(code), mi_attn_version(), mi_attn_last_hip_error();
 
 plus forward(q, k, v, ...) -> (out, lse) and decode(q, k, v, ...) ->
@@ -89,6 +92,9 @@ def _load():
     lib.mi_attn_rotary.restype = ctypes.c_int
     lib.mi_attn_rotary.argtypes = [P, ctypes.c_int, i32, i32, i32, i32, S, P, P,
                                    ctypes.c_int64, i32, ctypes.c_double, i32, P]
+    lib.mi_attn_rotary_qk.restype = ctypes.c_int
+    lib.mi_attn_rotary_qk.argtypes = [P, P, ctypes.c_int, i32, i32, i32, i32, i32, S, S, P, P,
+                                      ctypes.c_int64, i32, ctypes.c_double, i32, P]
     lib.mi_attn_status_string.restype = ctypes.c_char_p
     lib.mi_attn_status_string.argtypes = [ctypes.c_int]
     lib.mi_attn_version.restype = i32
@@ -362,6 +368,47 @@ def mi_attn_rotary(x, rotary_dim=None, *, base=10000.0, interleaved=False,
         detail = f"hipError {mi_attn_last_hip_error()}" if st == 7 else ""
         raise MiAttnError(st, detail)
     return x
+
+
+def mi_attn_rotary_qk(q, k, rotary_dim=None, *, base=10000.0, interleaved=False,
+                      position_offset=0, position_offsets=None, cu_seqlens=None,
+                      max_seqlen=None, layout="bhsd", stream=None):
+    """Rotary embedding of q and k in place, one launch (the result of
+    mi_attn_rotary on each).  q and k share the layout, the rows and the
+    positions; their head counts may differ."""
+    packed = cu_seqlens is not None
+    for t in (k, position_offsets, cu_seqlens):
+        if t is not None and (not t.is_cuda or t.device != q.device):
+            raise MiAttnError(6, "every tensor must be on q's GPU device")
+    for t in (position_offsets, cu_seqlens):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise MiAttnError(3, "position_offsets / cu_seqlens must be contiguous int32")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype:
+        raise MiAttnError(4, f"{q.dtype} / {k.dtype}")
+    d = q.shape[-1]
+    if k.shape[-1] != d:
+        raise MiAttnError(2, "q and k head dims differ")
+    rd = d if rotary_dim is None else int(rotary_dim)
+    if packed:
+        bsz, hq, hkv, seqlen = cu_seqlens.numel() - 1, q.shape[1], k.shape[1], int(max_seqlen)
+    elif layout == "bhsd":
+        bsz, hq, hkv, seqlen = q.shape[0], q.shape[1], k.shape[1], q.shape[2]
+    else:
+        bsz, hq, hkv, seqlen = q.shape[0], q.shape[2], k.shape[2], q.shape[1]
+    if not packed and (k.shape[0] != bsz or k.shape[2 if layout == "bhsd" else 1] != seqlen):
+        raise MiAttnError(2, "q and k rows differ")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    qs = _strides(q, layout, packed)
+    ks = _strides(k, layout, packed)
+    st = _lib.mi_attn_rotary_qk(_ptr(q), _ptr(k), _DTYPE_CODE[q.dtype], bsz, hq, hkv, seqlen, d,
+                                ctypes.byref(qs), ctypes.byref(ks), _ptr(cu_seqlens),
+                                _ptr(position_offsets), int(position_offset), rd, float(base),
+                                int(bool(interleaved)), ctypes.c_void_p(stream))
+    if st != 0:
+        detail = f"hipError {mi_attn_last_hip_error()}" if st == 7 else ""
+        raise MiAttnError(st, detail)
+    return q, k
 
 
 def _check_cu(cu, max_len, rows):

@@ -71,10 +71,13 @@ struct DecParams {
 // (freq_pi[k] = base^(-2k / rotary_dim) / pi, computed in double on the host).
 struct RopeParams {
     void* x;
+    void* x2;                        // a second tensor (K) with the same rows, or null
     const int32_t* cu_seqlens;       // packed x [T, H, d], or null (dense)
     const int32_t* offsets;          // per-sequence position offsets, or null
     int64_t sb, sh, sr;              // element strides (batch unused when packed)
+    int64_t sb2, sh2, sr2;           // those of x2
     int32_t batch, heads, seqlen;    // seqlen: rows per sequence (packed: the maximum)
+    int32_t heads2;                  // heads of x2 (0 without it)
     int32_t rotary_dim;              // a multiple of 16, <= head dim
     int32_t interleaved;             // 0: pairs (k, k + rd/2); 1: pairs (2k, 2k + 1)
     int64_t offset;

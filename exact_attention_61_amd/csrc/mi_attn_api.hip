@@ -348,6 +348,70 @@ mi_attn_status_t decode(const void* q, const void* k, const void* v, void* o, fl
 
 }  // namespace
 
+namespace {
+
+// Rotary embedding of x (and of x2 with heads2 > 0, the same rows and
+// positions) in one launch; the checks of mi_attn_rotary and
+// mi_attn_rotary_qk in their documented order.
+mi_attn_status_t rotary(void* x, void* x2, mi_attn_dtype_t dtype, int32_t batch, int32_t heads,
+                        int32_t heads2, int32_t seqlen, int32_t head_dim,
+                        const mi_attn_strides_t* strides, const mi_attn_strides_t* strides2,
+                        const int32_t* cu_seqlens, const int32_t* position_offsets,
+                        int64_t position_offset, int32_t rotary_dim, double base,
+                        int32_t interleaved, struct ihipStream_t* stream) {
+    if (dtype != MI_ATTN_F16 && dtype != MI_ATTN_BF16) return MI_ATTN_ERR_DTYPE;
+    if (batch < 0 || heads < 1 || heads2 < 0 || seqlen < 0 || head_dim < 1)
+        return MI_ATTN_ERR_SHAPE;
+    // grid y (batch) and z (groups of 4 heads of each tensor)
+    if (batch > 65535 || (heads + 3) / 4 + (heads2 + 3) / 4 > 65535) return MI_ATTN_ERR_SHAPE;
+    if (rotary_dim < 16 || rotary_dim % 16 != 0 || rotary_dim > head_dim || rotary_dim > 256)
+        return MI_ATTN_ERR_UNSUPPORTED;
+    if (!std::isfinite(base) || base <= 0.0) return MI_ATTN_ERR_ARG;
+    if (interleaved != 0 && interleaved != 1) return MI_ATTN_ERR_ARG;
+    if (batch == 0 || seqlen == 0) return MI_ATTN_OK;
+    const bool two = heads2 > 0;
+    if (x == nullptr || (two && x2 == nullptr)) return MI_ATTN_ERR_NULL;
+    const bool packed = cu_seqlens != nullptr;
+    const mi_attn_strides_t xs = strides ? *strides : default_strides(packed, heads, seqlen, head_dim);
+    const mi_attn_strides_t xs2 =
+        strides2 ? *strides2 : default_strides(packed, heads2, seqlen, head_dim);
+    if (!stride_ok(xs) || !aligned16(x)) return MI_ATTN_ERR_LAYOUT;
+    if (two && (!stride_ok(xs2) || !aligned16(x2) || x2 == x)) return MI_ATTN_ERR_LAYOUT;
+    // rows and heads may not overlap (a thread writes its features of every head)
+    if ((seqlen > 1 || packed) && (xs.row < head_dim || (two && xs2.row < head_dim)))
+        return MI_ATTN_ERR_LAYOUT;
+    if ((heads > 1 && xs.head < head_dim) || (heads2 > 1 && xs2.head < head_dim))
+        return MI_ATTN_ERR_LAYOUT;
+
+    mi_attn::RopeParams p{};
+    p.x = x;
+    p.x2 = two ? x2 : nullptr;
+    p.cu_seqlens = cu_seqlens;
+    p.offsets = position_offsets;
+    p.sb = xs.batch; p.sh = xs.head; p.sr = xs.row;
+    p.sb2 = xs2.batch; p.sh2 = xs2.head; p.sr2 = xs2.row;
+    p.batch = batch;
+    p.heads = heads;
+    p.heads2 = two ? heads2 : 0;
+    p.seqlen = seqlen;
+    p.rotary_dim = rotary_dim;
+    p.interleaved = interleaved;
+    p.offset = position_offset;
+    // pair k turns by base^(-2k / rd) radians per position, i.e.
+    // base^(-2k / rd) / pi half-turns
+    const double lb = std::log(base);
+    for (int k2 = 0; k2 < rotary_dim / 2; ++k2)
+        p.freq_pi[k2] = std::exp(-2.0 * k2 / rotary_dim * lb) / 3.14159265358979323846;
+    const hipError_t err = mi_attn::launch_rotary(p, (int)dtype, reinterpret_cast<hipStream_t>(stream));
+    if (err != hipSuccess) {
+        g_last_hip_error = (int32_t)err;
+        return MI_ATTN_ERR_HIP;
+    }
+    return MI_ATTN_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t mi_attn_decode_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t lq,
@@ -459,44 +523,23 @@ mi_attn_status_t mi_attn_rotary(void* x, mi_attn_dtype_t dtype, int32_t batch,
                                 const int32_t* position_offsets, int64_t position_offset,
                                 int32_t rotary_dim, double base, int32_t interleaved,
                                 struct ihipStream_t* stream) {
-    if (dtype != MI_ATTN_F16 && dtype != MI_ATTN_BF16) return MI_ATTN_ERR_DTYPE;
-    if (batch < 0 || heads < 1 || seqlen < 0 || head_dim < 1) return MI_ATTN_ERR_SHAPE;
-    if (batch > 65535 || heads > 65535 * 4) return MI_ATTN_ERR_SHAPE;   // grid y and z
-    if (rotary_dim < 16 || rotary_dim % 16 != 0 || rotary_dim > head_dim || rotary_dim > 256)
-        return MI_ATTN_ERR_UNSUPPORTED;
-    if (!std::isfinite(base) || base <= 0.0) return MI_ATTN_ERR_ARG;
-    if (interleaved != 0 && interleaved != 1) return MI_ATTN_ERR_ARG;
-    if (batch == 0 || seqlen == 0) return MI_ATTN_OK;
-    if (x == nullptr) return MI_ATTN_ERR_NULL;
-    const bool packed = cu_seqlens != nullptr;
-    const mi_attn_strides_t xs = strides ? *strides : default_strides(packed, heads, seqlen, head_dim);
-    if (!stride_ok(xs) || !aligned16(x)) return MI_ATTN_ERR_LAYOUT;
-    // rows and heads may not overlap (a thread writes its features of every head)
-    if ((seqlen > 1 || packed) && xs.row < head_dim) return MI_ATTN_ERR_LAYOUT;
-    if (heads > 1 && xs.head < head_dim) return MI_ATTN_ERR_LAYOUT;
+    return rotary(x, nullptr, dtype, batch, heads, 0, seqlen, head_dim, strides, nullptr,
+                  cu_seqlens, position_offsets, position_offset, rotary_dim, base, interleaved,
+                  stream);
+}
 
-    mi_attn::RopeParams p{};
-    p.x = x;
-    p.cu_seqlens = cu_seqlens;
-    p.offsets = position_offsets;
-    p.sb = xs.batch; p.sh = xs.head; p.sr = xs.row;
-    p.batch = batch;
-    p.heads = heads;
-    p.seqlen = seqlen;
-    p.rotary_dim = rotary_dim;
-    p.interleaved = interleaved;
-    p.offset = position_offset;
-    // pair k turns by base^(-2k / rd) radians per position, i.e.
-    // base^(-2k / rd) / pi half-turns
-    const double lb = std::log(base);
-    for (int k2 = 0; k2 < rotary_dim / 2; ++k2)
-        p.freq_pi[k2] = std::exp(-2.0 * k2 / rotary_dim * lb) / 3.14159265358979323846;
-    const hipError_t err = mi_attn::launch_rotary(p, (int)dtype, reinterpret_cast<hipStream_t>(stream));
-    if (err != hipSuccess) {
-        g_last_hip_error = (int32_t)err;
-        return MI_ATTN_ERR_HIP;
-    }
-    return MI_ATTN_OK;
+mi_attn_status_t mi_attn_rotary_qk(void* q, void* k, mi_attn_dtype_t dtype, int32_t batch,
+                                   int32_t hq, int32_t hkv, int32_t seqlen, int32_t head_dim,
+                                   const mi_attn_strides_t* q_strides,
+                                   const mi_attn_strides_t* k_strides,
+                                   const int32_t* cu_seqlens, const int32_t* position_offsets,
+                                   int64_t position_offset, int32_t rotary_dim, double base,
+                                   int32_t interleaved, struct ihipStream_t* stream) {
+    if (hkv < 1) return dtype != MI_ATTN_F16 && dtype != MI_ATTN_BF16 ? MI_ATTN_ERR_DTYPE
+                                                                      : MI_ATTN_ERR_SHAPE;
+    return rotary(q, k, dtype, batch, hq, hkv, seqlen, head_dim, q_strides, k_strides,
+                  cu_seqlens, position_offsets, position_offset, rotary_dim, base, interleaved,
+                  stream);
 }
 
 const char* mi_attn_status_string(mi_attn_status_t status) {

@@ -10,10 +10,13 @@
 //
 // The pass is bound by HBM traffic (each rotated element read and written
 // once).  A thread owns 8 pairs of one position in 4 heads (grid z picks
-// the heads): it forms the 8 angles once -- in double, reduced to [0, 2)
-// half-turns before the single-precision sine and cosine, so positions in
-// the millions keep full accuracy -- and rotates those pairs in its heads
-// with 16-byte loads and stores.
+// the heads; with a second tensor, Q then K, both in one launch): it issues
+// the 16-byte loads of its pairs, forms the 8 angles while they are in
+// flight -- in double, reduced to [0, 2) half-turns before the
+// single-precision sine and cosine, so positions in the millions keep full
+// accuracy -- and rotates the pairs.  (Non-temporal loads and stores were
+// measured: faster on a 40 MiB Q+K rotated again and again, slower on
+// 160 MiB; plain ones are kept.)
 #include "common.hpp"
 
 namespace mi_attn {
@@ -64,83 +67,92 @@ __global__ __launch_bounds__(kRopeThreads) void rotary_kernel(RopeParams p) {
     if (t >= len) return;
     const int64_t pos = p.offset + (p.offsets != nullptr ? p.offsets[b] : 0) + t;
 
-    float cs[8], sn[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const double a = (double)pos * p.freq_pi[8 * c + j];   // half-turns
-        const double r = a - 2.0 * __builtin_floor(a * 0.5);   // in [0, 2)
-        sincospif((float)r, &sn[j], &cs[j]);
-    }
+    // grid z: the head groups of x, then those of x2
+    const int zx = (p.heads + kRopeHeadBatch - 1) / kRopeHeadBatch;
+    const bool second = (int)blockIdx.z >= zx;
+    const int h0 = ((int)blockIdx.z - (second ? zx : 0)) * kRopeHeadBatch;
+    const int heads = second ? p.heads2 : p.heads;
+    const int64_t sb = second ? p.sb2 : p.sb, sh = second ? p.sh2 : p.sh,
+                  sr = second ? p.sr2 : p.sr;
 
     // the two 16-byte chunks of this thread: NeoX features 8c.. and
     // rd/2 + 8c..; GPT-J features 16c.. and 16c + 8..
     const int f0 = INTERLEAVED ? 16 * c : 8 * c;
     const int f1 = INTERLEAVED ? 16 * c + 8 : p.rotary_dim / 2 + 8 * c;
-    uint16_t* base = reinterpret_cast<uint16_t*>(p.x) +
-                     (p.cu_seqlens != nullptr ? 0 : (int64_t)b * p.sb) + (row0 + t) * p.sr;
+    uint16_t* base = reinterpret_cast<uint16_t*>(second ? p.x2 : p.x) +
+                     (p.cu_seqlens != nullptr ? 0 : (int64_t)b * sb) + (row0 + t) * sr;
 
-    {
-        const int h0 = (int)blockIdx.z * kRopeHeadBatch;
-        u32x4_t a[kRopeHeadBatch], d[kRopeHeadBatch];
+    // loads first: the angles below are computed while they are in flight
+    u32x4_t a[kRopeHeadBatch], d[kRopeHeadBatch];
 #pragma unroll
-        for (int i = 0; i < kRopeHeadBatch; ++i) {
-            if (h0 + i < p.heads) {
-                const uint16_t* r = base + (int64_t)(h0 + i) * p.sh;
-                a[i] = *reinterpret_cast<const u32x4_t*>(r + f0);
-                d[i] = *reinterpret_cast<const u32x4_t*>(r + f1);
-            }
+    for (int i = 0; i < kRopeHeadBatch; ++i) {
+        if (h0 + i < heads) {
+            const uint16_t* r = base + (int64_t)(h0 + i) * sh;
+            a[i] = *reinterpret_cast<const u32x4_t*>(r + f0);
+            d[i] = *reinterpret_cast<const u32x4_t*>(r + f1);
         }
+    }
+
+    float cs[8], sn[8];
 #pragma unroll
-        for (int i = 0; i < kRopeHeadBatch; ++i) {
-            if (h0 + i >= p.heads) continue;
-            float x[8], y[8];               // pair j = (x[j], y[j])
-            if (INTERLEAVED) {
+    for (int j = 0; j < 8; ++j) {
+        const double ang = (double)pos * p.freq_pi[8 * c + j];   // half-turns
+        const double r = ang - 2.0 * __builtin_floor(ang * 0.5);  // in [0, 2)
+        sincospif((float)r, &sn[j], &cs[j]);
+    }
+
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    x[j] = chunk_elem<T>(a[i], 2 * j);
-                    y[j] = chunk_elem<T>(a[i], 2 * j + 1);
-                    x[4 + j] = chunk_elem<T>(d[i], 2 * j);
-                    y[4 + j] = chunk_elem<T>(d[i], 2 * j + 1);
-                }
-            } else {
+    for (int i = 0; i < kRopeHeadBatch; ++i) {
+        if (h0 + i >= heads) continue;
+        float x[8], y[8];               // pair j = (x[j], y[j])
+        if (INTERLEAVED) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    x[j] = chunk_elem<T>(a[i], j);
-                    y[j] = chunk_elem<T>(d[i], j);
-                }
+            for (int j = 0; j < 4; ++j) {
+                x[j] = chunk_elem<T>(a[i], 2 * j);
+                y[j] = chunk_elem<T>(a[i], 2 * j + 1);
+                x[4 + j] = chunk_elem<T>(d[i], 2 * j);
+                y[4 + j] = chunk_elem<T>(d[i], 2 * j + 1);
             }
-            float xr[8], yr[8];
+        } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                xr[j] = x[j] * cs[j] - y[j] * sn[j];
-                yr[j] = x[j] * sn[j] + y[j] * cs[j];
+                x[j] = chunk_elem<T>(a[i], j);
+                y[j] = chunk_elem<T>(d[i], j);
             }
-            u32x4_t oa, od;
-            if (INTERLEAVED) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    oa[j] = Elem<T>::put(xr[j], yr[j]);
-                    od[j] = Elem<T>::put(xr[4 + j], yr[4 + j]);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    oa[j] = Elem<T>::put(xr[2 * j], xr[2 * j + 1]);
-                    od[j] = Elem<T>::put(yr[2 * j], yr[2 * j + 1]);
-                }
-            }
-            uint16_t* r = base + (int64_t)(h0 + i) * p.sh;
-            *reinterpret_cast<u32x4_t*>(r + f0) = oa;
-            *reinterpret_cast<u32x4_t*>(r + f1) = od;
         }
+        float xr[8], yr[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            xr[j] = x[j] * cs[j] - y[j] * sn[j];
+            yr[j] = x[j] * sn[j] + y[j] * cs[j];
+        }
+        u32x4_t oa, od;
+        if (INTERLEAVED) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                oa[j] = Elem<T>::put(xr[j], yr[j]);
+                od[j] = Elem<T>::put(xr[4 + j], yr[4 + j]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                oa[j] = Elem<T>::put(xr[2 * j], xr[2 * j + 1]);
+                od[j] = Elem<T>::put(yr[2 * j], yr[2 * j + 1]);
+            }
+        }
+        uint16_t* r = base + (int64_t)(h0 + i) * sh;
+        *reinterpret_cast<u32x4_t*>(r + f0) = oa;
+        *reinterpret_cast<u32x4_t*>(r + f1) = od;
     }
 }
 
 template <typename T>
 hipError_t launch_rotary_t(const RopeParams& p, hipStream_t stream) {
     const int64_t units = (int64_t)p.seqlen * (p.rotary_dim / 16);
+    const int z = (p.heads + kRopeHeadBatch - 1) / kRopeHeadBatch +
+                  (p.heads2 + kRopeHeadBatch - 1) / kRopeHeadBatch;
     const dim3 grid((unsigned)((units + kRopeThreads - 1) / kRopeThreads), (unsigned)p.batch,
-                    (unsigned)((p.heads + kRopeHeadBatch - 1) / kRopeHeadBatch));
+                    (unsigned)z);
     if (p.interleaved)
         hipLaunchKernelGGL((rotary_kernel<T, true>), grid, dim3(kRopeThreads), 0, stream, p);
     else

@@ -342,7 +342,7 @@ MI_ATTN_API mi_attn_status_t mi_attn_fwd_dropout(const void* q, const void* k, c
  *
  * Ownership: the caller owns x, cu_seqlens and position_offsets; nothing is
  * retained.  Errors: a dtype other than F16/BF16 -> MI_ATTN_ERR_DTYPE; a
- * negative size or batch > 65535 -> MI_ATTN_ERR_SHAPE; an unsupported
+ * negative size, batch > 65535 or heads > 4 * 65535 -> MI_ATTN_ERR_SHAPE; an unsupported
  * rotary_dim -> MI_ATTN_ERR_UNSUPPORTED; base not finite and positive or
  * interleaved not 0/1 -> MI_ATTN_ERR_ARG; x not 16-byte aligned, strides
  * not multiples of 8 elements, or rows/heads that overlap ->
@@ -357,6 +357,30 @@ MI_ATTN_API mi_attn_status_t mi_attn_rotary(void* x, mi_attn_dtype_t dtype, int3
                                             int64_t position_offset, int32_t rotary_dim,
                                             double base, int32_t interleaved,
                                             struct ihipStream_t* stream);
+
+/*
+ * mi_attn_rotary_qk -- mi_attn_rotary of Q and K together, in one launch.
+ *
+ * The same tutorial section applies the embedding to both Q and K at the
+ * same positions.  q is [batch, hq, seqlen, head_dim] and k is [batch, hkv,
+ * seqlen, head_dim] (each through its own strides, NULL: contiguous), or
+ * both packed [T, hq | hkv, head_dim] with the shared cu_seqlens; positions,
+ * rotary_dim, base and interleaved as for mi_attn_rotary, and the result is
+ * that of mi_attn_rotary on q and then on k.  q and k must not overlap in
+ * memory (q == k is rejected with MI_ATTN_ERR_LAYOUT).  hkv < 1 ->
+ * MI_ATTN_ERR_SHAPE; every other check, ownership and error rule as for
+ * mi_attn_rotary, applied to both tensors.
+ */
+MI_ATTN_API mi_attn_status_t mi_attn_rotary_qk(void* q, void* k, mi_attn_dtype_t dtype,
+                                               int32_t batch, int32_t hq, int32_t hkv,
+                                               int32_t seqlen, int32_t head_dim,
+                                               const mi_attn_strides_t* q_strides,
+                                               const mi_attn_strides_t* k_strides,
+                                               const int32_t* cu_seqlens,
+                                               const int32_t* position_offsets,
+                                               int64_t position_offset, int32_t rotary_dim,
+                                               double base, int32_t interleaved,
+                                               struct ihipStream_t* stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 MI_ATTN_API const char* mi_attn_status_string(mi_attn_status_t status);

@@ -31,7 +31,8 @@ def test_exports_every_declared_function():
     assert set(names) == {"mi_attn_fwd", "mi_attn_fwd_select", "mi_attn_decode",
                           "mi_attn_decode_noalloc", "mi_attn_decode_noalloc_max_bytes",
                           "mi_attn_decode_workspace_size", "mi_attn_decode_splits",
-                          "mi_attn_rotary", "mi_attn_fwd_dropout", "mi_attn_status_string",
+                          "mi_attn_rotary", "mi_attn_rotary_qk", "mi_attn_fwd_dropout",
+                          "mi_attn_status_string",
                           "mi_attn_version",
                           "mi_attn_last_hip_error"}
     for n in names:
@@ -204,6 +205,31 @@ def test_rotary_rejected_before_any_hip_call(kw, code):
 def test_rotary_empty_is_noop():
     assert rcall(x=None, b=0) == 0
     assert rcall(x=None, l=0) == 0
+
+
+def qkcall(q=A, k=A * 2, dt=1, b=2, hq=8, hkv=2, l=100, d=128, qs=None, ks=None, cu=None,
+           offs=None, off=0, rd=128, base=10000.0, inter=0):
+    ref = lambda s: None if s is None else ctypes.byref(s)
+    return mi.lib().mi_attn_rotary_qk(q, k, dt, b, hq, hkv, l, d, ref(qs), ref(ks), cu, offs, off,
+                                      rd, base, inter, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(dt=2), 4), (dict(dt=2, hkv=0), 4),
+    (dict(hkv=0), 2), (dict(hq=0), 2), (dict(b=70000), 2), (dict(l=-1), 2),
+    (dict(hq=65535 * 4, hkv=8), 2),                              # grid z of both tensors
+    (dict(rd=24), 5), (dict(base=0.0), 6), (dict(inter=3), 6),
+    (dict(k=A), 3),                                              # the same tensor twice
+    (dict(k=A * 2 + 8), 3), (dict(ks=Strides(0, 128, 60)), 3),
+    (dict(ks=Strides(0, 64, 512)), 3), (dict(qs=Strides(0, 128 * 100, 64)), 3),
+])
+def test_rotary_qk_rejected_before_any_hip_call(kw, code):
+    assert qkcall(**kw) == code
+
+
+def test_rotary_qk_empty_is_noop():
+    assert qkcall(q=None, k=None, b=0) == 0
+    assert qkcall(q=None, k=None, l=0) == 0
 
 
 def test_decode_workspace_plan():

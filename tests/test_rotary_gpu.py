@@ -131,3 +131,63 @@ def test_rotary_then_attention(causal):
     o_ref, l_ref = oracle.attention(qr, kr, f64(v), causal=causal)
     compare(o.to("cpu", torch.float64).numpy(), lse.to("cpu", torch.float64).numpy(),
             o_ref, l_ref)
+
+
+# mi_attn_rotary_qk: Q and K in one launch, each against the oracle's
+# rotation of that tensor (the same bound), with its own head count.
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("inter", [False, True])
+@pytest.mark.parametrize("hq,hkv,d,rd", [(8, 2, 128, 128), (5, 3, 64, 32), (32, 8, 128, 64),
+                                         (1, 1, 64, 64)])
+def test_rotary_qk_dense(dtype, inter, hq, hkv, d, rd):
+    import exact_attention_61_amd as mi
+    note(f"rotary qk {dtype} interleaved {inter} hq {hq} hkv {hkv} d {d} rd {rd}")
+    q = rand((2, hq, 129, d), dtype, seed=20 + hq)
+    k = rand((2, hkv, 129, d), dtype, seed=30 + hkv)
+    qg, kg = q.cuda(), k.cuda()
+    mi.mi_attn_rotary_qk(qg, kg, rd, interleaved=inter, position_offset=5)
+    torch.cuda.synchronize()
+    f64 = workloads.to_f64
+    check(qg, oracle.rotate_dense(f64(q), rd, 10000.0, inter, offset=5), dtype)
+    check(kg, oracle.rotate_dense(f64(k), rd, 10000.0, inter, offset=5), dtype)
+    assert torch.equal(qg[..., rd:].cpu(), q[..., rd:])
+    assert torch.equal(kg[..., rd:].cpu(), k[..., rd:])
+
+
+def test_rotary_qk_matches_two_calls_bitwise():
+    """One launch over Q and K gives exactly the results of mi_attn_rotary on
+    each: the same arithmetic per element."""
+    import exact_attention_61_amd as mi
+    note("rotary qk against two single calls")
+    q = rand((1, 32, 1000, 128), BF16, seed=40).cuda()
+    k = rand((1, 8, 1000, 128), BF16, seed=41).cuda()
+    q1, k1 = q.clone(), k.clone()
+    mi.mi_attn_rotary_qk(q, k, 128, position_offset=123)
+    mi.mi_attn_rotary(q1, 128, position_offset=123)
+    mi.mi_attn_rotary(k1, 128, position_offset=123)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q1) and torch.equal(k, k1)
+
+
+@pytest.mark.parametrize("inter", [False, True])
+def test_rotary_qk_packed_bshd_view(inter):
+    """Packed Q and K that are views into one [T, 3, H, d] QKV tensor: Q and K
+    rotated, V and the rows past every sequence untouched."""
+    import exact_attention_61_amd as mi
+    lens = [7, 0, 250, 1]
+    note(f"rotary qk packed qkv view {lens} interleaved {inter}")
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    total = int(cu[-1])
+    qkv = rand((total + 3, 3, 4, 64), F16, seed=42)
+    offs = [1, 2, 3, 70000]
+    g = qkv.cuda()
+    mi.mi_attn_rotary_qk(g[:, 0], g[:, 1], 64, interleaved=inter,
+                         position_offsets=torch.tensor(offs, dtype=torch.int32, device="cuda"),
+                         cu_seqlens=cu.cuda(), max_seqlen=max(lens))
+    torch.cuda.synchronize()
+    f64 = workloads.to_f64
+    for i in (0, 1):
+        ref = oracle.rotate_packed(f64(qkv[:, i]), cu.numpy(), 64, 10000.0, inter, offsets=offs)
+        check(g[:, i], ref, F16)
+        assert torch.equal(g[total:, i].cpu(), qkv[total:, i])
+    assert torch.equal(g[:, 2].cpu(), qkv[:, 2])
