@@ -427,16 +427,25 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     // is normalised by the fp32 sums of the probabilities before dropout,
     // so the rounding of P does not cancel as it does with the rounded sums.
     constexpr bool kSplitAll = Mma<Tin>::kSplit && DROP;
-    // Dropout mask of part g4 (scores 4 g4 .. 4 g4 + 3 of row block rb) of
-    // tile kt: keys kt*BN + 32 kq + 4 hi + 8 g4 + i, i = 0..3, one Philox
-    // call on counter (key / 4, sequence row, head, sequence).  Kept
-    // probabilities are scaled by 1 / (1 - p), dropped ones are 0.
-    auto drop4 = [&](int kt, int rb, int g4, float (&x)[4]) {
-        uint32_t c[4] = {(uint32_t)(kt * (BN / 4) + 8 * kq + hi + 2 * g4), (uint32_t)qrow(rb),
-                         (uint32_t)h, (uint32_t)b};
+    // Dropout.  Part g4 of row block rb of tile kt holds the scores of keys
+    // kt*BN + 32 kq + 4 hi + 8 g4 + i (i = 0..3).  One Philox call on counter
+    // (2 (key / 16) + (key / 4) % 2, sequence row, head, sequence) gives 8
+    // 16-bit halves, which decide this lane's 8 keys of a 16-key group:
+    // parts g4 and g4 + 1 for even g4 (words 0, 1 and words 2, 3).
+    auto drop_words = [&](int kt, int rb, int g4, uint32_t (&c)[4]) {
+        c[0] = (uint32_t)(2 * (kt * (BN / 16) + 2 * kq + (g4 >> 1)) + hi);
+        c[1] = (uint32_t)qrow(rb);
+        c[2] = (uint32_t)h;
+        c[3] = (uint32_t)b;
         philox4x32_10(c, p.seed_lo, p.seed_hi);
+    };
+    // key i of a part is kept iff half i of (w0, w1) is at least the
+    // threshold; kept probabilities are scaled by 1 / (1 - p), dropped ones
+    // are 0
+    auto drop_apply = [&](uint32_t w0, uint32_t w1, float (&x)[4]) {
+        const uint32_t u[4] = {w0 & 0xffffu, w0 >> 16, w1 & 0xffffu, w1 >> 16};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = c[i] >= p.drop_threshold ? x[i] * p.drop_scale : 0.0f;
+        for (int i = 0; i < 4; ++i) x[i] = u[i] >= p.drop_threshold ? x[i] * p.drop_scale : 0.0f;
     };
     // PV of the last tile; LO: it was a masked tile, so for bf16 its P was
     // split and the low part goes in too
@@ -542,6 +551,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
             // group g exponentiates and sums part g and rounds part g - 1.
             // The row sums go straight into l (fp32) and, for bf16, lr.
             float pe[2][4];              // probabilities of the last two parts
+            uint32_t dw[4];              // dropout words of the current part pair
 #pragma unroll
             for (int gi = 0; gi < kGroups; ++gi) {
                 vread_at(gi);
@@ -559,7 +569,11 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 if (gi >= 1) {
                     const int u = gi - 1, rb = u >> 2, c = (u >> 1) & 1, half = u & 1;
                     float (&x)[4] = pe[u & 1];
-                    if constexpr (DROP) drop4(j, rb, u & 3, x);
+                    if constexpr (DROP) {
+                        if ((u & 1) == 0) drop_words(j, rb, u & 3, dw);
+                        if ((u & 1) == 0) drop_apply(dw[0], dw[1], x);
+                        else drop_apply(dw[2], dw[3], x);
+                    }
                     uint32_t a, d, alo = 0, dlo = 0;
                     pack_pair(x[0], x[1], a, alo);
                     pack_pair(x[2], x[3], d, dlo);
@@ -588,6 +602,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         } else {
             float psum[2][4];
             float rsr[2][2];             // row sums of the rounded P, per chunk
+            uint32_t dw[2][4];           // dropout words of each row block's part pair
             bool upd;                    // some reference moved (wave-uniform)
             float alpha[2] = {1.0f, 1.0f};
 #pragma unroll
@@ -637,7 +652,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                     psum[rb][(gi - 1) >> 1] = (pe[0] + pe[1]) + (pe[2] + pe[3]);
                     pin(psum[rb][(gi - 1) >> 1]);
                     if constexpr (DROP) {
-                        drop4(j, rb, (gi - 1) >> 1, pe);
+                        const int g4 = (gi - 1) >> 1;
+                        if ((g4 & 1) == 0) drop_words(j, rb, g4, dw[rb]);
+                        if ((g4 & 1) == 0) drop_apply(dw[rb][0], dw[rb][1], pe);
+                        else drop_apply(dw[rb][2], dw[rb][3], pe);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) s_cur[rb][e0 + i] = pe[i];
                     }

@@ -30,9 +30,9 @@ struct FwdParams {
     int32_t causal;
     int32_t causal_pairs;            // causal q-tile order (0, 1, 2; -1 default)
     int32_t n_cu;                    // compute units of the device
-    // dropout on P (the dropout kernels only): a key is kept iff its Philox
-    // word is at least drop_threshold = floor(p * 2^32); kept probabilities
-    // are multiplied by drop_scale = 1 / (1 - p)
+    // dropout on P (the dropout kernels only): a key is kept iff its 16-bit
+    // half of a Philox word is at least drop_threshold = floor(p * 2^16);
+    // kept probabilities are multiplied by drop_scale = 1 / (1 - p)
     uint32_t drop_threshold;
     float drop_scale;
     uint32_t seed_lo, seed_hi;       // the Philox key

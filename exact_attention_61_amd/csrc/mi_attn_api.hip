@@ -151,10 +151,10 @@ mi_attn_status_t forward(const void* q, const void* k, const void* v,
     p.causal = causal;
     p.causal_pairs = causal_order;
     p.n_cu = current_device_cus();
-    // dropout: keep a key iff its Philox word >= floor(p * 2^32); kept
+    // dropout: keep a key iff its 16-bit Philox half >= floor(p * 2^16); kept
     // probabilities are scaled by 1 / (1 - p)
     const bool drop = dropout_p > 0.0;
-    p.drop_threshold = (uint32_t)std::floor(dropout_p * 4294967296.0);
+    p.drop_threshold = (uint32_t)std::floor(dropout_p * 65536.0);
     p.drop_scale = (float)(1.0 / (1.0 - dropout_p));
     p.seed_lo = (uint32_t)(seed & 0xffffffffu);
     p.seed_hi = (uint32_t)(seed >> 32);

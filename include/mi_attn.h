@@ -291,9 +291,12 @@ MI_ATTN_API int32_t mi_attn_decode_splits(int32_t batch, int32_t hq, int32_t hkv
  *
  * The mask: Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random
  * numbers: as easy as 1, 2, 3", SC 2011) with key (seed & 0xffffffff,
- * seed >> 32) on counter (j / 4, i, h, b) -- key j, query row i within its
- * sequence, query head h, batch entry (packed: sequence) b; output word
- * j % 4 keeps key j iff it is at least floor(dropout_p * 2^32).  The same
+ * seed >> 32) on counter (2 (j / 16) + (j / 4) % 2, i, h, b) -- key j,
+ * query row i within its sequence, query head h, batch entry (packed:
+ * sequence) b.  The four output words are read as eight 16-bit halves (half
+ * 2m = low 16 bits of word m, half 2m + 1 = its high 16 bits); key j takes
+ * half 4 ((j / 8) % 2) + j % 4 and is kept iff that half is at least
+ * floor(dropout_p * 2^16) (dropout_p is resolved to 2^-16).  The same
  * (seed, b, h, i, j) always gives the same decision, whatever the layout or
  * the launch.
  *

@@ -24,6 +24,7 @@ from .rotary import (  # noqa: F401
 from .dropout import (  # noqa: F401
     attention_dropout,
     drop_threshold,
+    keep_halves,
     keep_mask,
     philox4x32_10,
 )

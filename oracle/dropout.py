@@ -17,11 +17,15 @@ generator with a published definition:
   itself (dropout comes after the normalisation).
 * M[i, j] comes from Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel
   random numbers: as easy as 1, 2, 3", SC 2011): key = the 64-bit seed as
-  (low word, high word); counter = (j // 4, i, h, b) for batch (sequence) b,
-  query head h, query row i (within its sequence) and key j; of the four
-  output words, word j % 4 decides key j.  The key is kept iff that word is
-  at least floor(p * 2^32) (an integer comparison, so both sides decide
-  alike).
+  (low word, high word); counter = (2 (j // 16) + (j // 4) % 2, i, h, b) for
+  batch (sequence) b, query head h, query row i (within its sequence) and
+  key j.  The four output words are read as eight 16-bit halves, half 2m
+  the low and half 2m + 1 the high half of word m; key j takes half
+  4 ((j // 8) % 2) + j % 4.  So one call decides 8 keys of a 16-key group
+  (offsets 0-3 and 8-11, or 4-7 and 12-15), and every key of the group has
+  its own half.  The key is kept iff its half is at least floor(p * 2^16)
+  (an integer comparison, so both sides decide alike; p is resolved to
+  2^-16).
 
 Parity pinned by the generator's published known-answer vectors, by p = 0
 reducing to the plain attention, and statistically (keep fraction, mean
@@ -61,21 +65,34 @@ def philox4x32_10(counters, key):
 
 
 def drop_threshold(p):
-    """floor(p * 2^32): a key is kept iff its word is at least this."""
+    """floor(p * 2^16): a key is kept iff its 16-bit half is at least this."""
     if not 0.0 <= p < 1.0:
         raise ValueError("dropout probability must be in [0, 1)")
-    return int(math.floor(float(p) * 4294967296.0))
+    return int(math.floor(float(p) * 65536.0))
+
+
+def keep_halves(seed, b, h, rows, lk):
+    """uint16 [len(rows), lk]: the Philox half that decides each key."""
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(lk, dtype=np.int64)
+    cidx = 2 * (j // 16) + (j // 4) % 2                  # counter word 0 of key j
+    half = 4 * ((j // 8) % 2) + j % 4                    # which of its 8 halves
+    n_ctr = 2 * ((lk + 15) // 16)
+    cc, ii = np.meshgrid(np.arange(n_ctr, dtype=np.int64), rows)   # [R, n_ctr]
+    ctr = np.stack([cc.ravel(), ii.ravel(), np.full(cc.size, h), np.full(cc.size, b)], axis=1)
+    key = (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    words = philox4x32_10(ctr, key).reshape(len(rows), n_ctr, 4).astype(np.uint32)
+    halves = np.empty((len(rows), n_ctr, 8), dtype=np.uint16)
+    halves[..., 0::2] = (words & 0xFFFF).astype(np.uint16)
+    halves[..., 1::2] = (words >> 16).astype(np.uint16)
+    return halves[:, cidx, half]
 
 
 def keep_mask(seed, b, h, rows, lk, p):
     """Boolean [len(rows), lk]: keys kept for query rows `rows` of (b, h)."""
-    rows = np.asarray(rows, dtype=np.int64)
-    n4 = (lk + 3) // 4
-    jj, ii = np.meshgrid(np.arange(n4, dtype=np.int64), rows)      # [R, n4]
-    ctr = np.stack([jj.ravel(), ii.ravel(), np.full(jj.size, h), np.full(jj.size, b)], axis=1)
-    key = (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
-    words = philox4x32_10(ctr, key).reshape(len(rows), n4 * 4)[:, :lk]
-    return words >= np.uint32(drop_threshold(p)) if lk else np.zeros((len(rows), 0), bool)
+    if lk == 0:
+        return np.zeros((len(np.asarray(rows)), 0), bool)
+    return keep_halves(seed, b, h, rows, lk) >= drop_threshold(p)
 
 
 def _attend_one_head_dropout(qh, kh, vh, scale, causal, p, seed, b, h, row_chunk):

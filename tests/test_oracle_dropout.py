@@ -33,8 +33,10 @@ def test_philox_known_answers(ctr, key, want):
 
 def test_threshold():
     assert oracle.drop_threshold(0.0) == 0
-    assert oracle.drop_threshold(0.5) == 2 ** 31
-    assert oracle.drop_threshold(0.25) == 2 ** 30
+    assert oracle.drop_threshold(0.5) == 2 ** 15
+    assert oracle.drop_threshold(0.25) == 2 ** 14
+    assert oracle.drop_threshold(0.1) == 6553
+    assert oracle.drop_threshold(1.0 - 2.0 ** -20) == 2 ** 16 - 1
     with pytest.raises(ValueError):
         oracle.drop_threshold(1.0)
     with pytest.raises(ValueError):
@@ -90,10 +92,32 @@ def test_mask_depends_only_on_its_coordinates():
     assert not np.array_equal(full, oracle.keep_mask(99, 3, 6, np.arange(64), 130, 0.2))
     assert not np.array_equal(full, oracle.keep_mask(99, 4, 5, np.arange(64), 130, 0.2))
     assert not np.array_equal(full, oracle.keep_mask(98, 3, 5, np.arange(64), 130, 0.2))
-    # word j % 4 of counter (j // 4, i, h, b) decides key j
-    w = oracle.philox4x32_10(np.array([[130 // 4 - 1, 7, 5, 3]], dtype=np.uint64), (99, 0))[0]
+    # keys 112..127 of row 7 (group 7): counter 14 decides offsets 0-3 and
+    # 8-11 by its 8 halves in order, counter 15 offsets 4-7 and 12-15; each
+    # half is the low then the high 16 bits of a word
     thr = oracle.drop_threshold(0.2)
-    assert [bool(x >= thr) for x in w] == list(full[7, 4 * (130 // 4 - 1):4 * (130 // 4)])
+    for c, offs in ((14, [0, 1, 2, 3, 8, 9, 10, 11]), (15, [4, 5, 6, 7, 12, 13, 14, 15])):
+        w = oracle.philox4x32_10(np.array([[c, 7, 5, 3]], dtype=np.uint64), (99, 0))[0]
+        halves = [int(x) >> s for x in w for s in (0, 16)]
+        halves = [x & 0xFFFF for x in halves]
+        assert [x >= thr for x in halves] == [bool(full[7, 112 + o]) for o in offs]
+
+
+def test_every_key_has_its_own_half():
+    """Within a row the (counter, half) pairs of distinct keys differ, and a
+    16-key group uses exactly two counters: no two keys share a decision."""
+    lk = 100
+    j = np.arange(lk)
+    cidx = 2 * (j // 16) + (j // 4) % 2
+    half = 4 * ((j // 8) % 2) + j % 4
+    pairs = set(zip(cidx.tolist(), half.tolist()))
+    assert len(pairs) == lk
+    for g in range(lk // 16):
+        assert set(cidx[16 * g:16 * g + 16].tolist()) == {2 * g, 2 * g + 1}
+    # the halves of one row are not all alike (a transposed or dropped
+    # index would repeat them)
+    hv = oracle.keep_halves(5, 0, 0, np.arange(3), lk)
+    assert len(set(hv[0].tolist())) > 90 and not np.array_equal(hv[0], hv[1])
 
 
 def test_packed_equals_dense_per_sequence():
