@@ -20,12 +20,12 @@
 // overflow is wrong: when a probability passes the 16-bit range (seen as an
 // inf or NaN accumulator for fp16, as an fp32 row sum past the largest bf16
 // for bf16), the work-group redoes the q-tile in a safe form that moves a
-// row's reference whenever a tile's max exceeds it by more than 2^8.  The row sums are taken in fp32 from the
-// unrounded probabilities.  For fp16 inputs they also normalise the output
-// (rounding P to fp16 moves the product by at most 2^-11 relative); for bf16
-// inputs the output is normalised by the sum of the probabilities as rounded
-// for the PV product (one v_dot2 per pair), so that the rounding of a
-// dominant probability cancels between numerator and denominator.
+// row's reference whenever a tile's max exceeds it by more than 2^8.  The
+// output is normalised by the fp32 sum of the probabilities as rounded for
+// the PV product (one v_dot2 per pair), so that the rounding of a dominant
+// probability cancels between numerator and denominator.  The log-sum-exp
+// takes the same sum for fp16 (the rounding moves it by less than 2^-11
+// relative) and, for bf16, an fp32 sum of the unrounded probabilities.
 //
 // Work decomposition.  A work-group of 4 waves owns BM = 128 query rows of
 // one (batch, head) at a time and walks the keys in tiles of BN = 64 keys.
@@ -423,6 +423,9 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 if (8 * (e >> 2) + (e & 3) > lim) s_cur[rb][e] = -__builtin_inff();
         }
     };
+    // fp16 without dropout: the row sums come from the rounded P only (lr);
+    // l takes their value after the last tile.
+    constexpr bool kSumsRounded = Mma<Tin>::kSumRounded && !DROP;
     // With dropout, bf16 P is split into hi + lo on every tile: the output
     // is normalised by the fp32 sums of the probabilities before dropout,
     // so the rounding of P does not cancel as it does with the rounded sums.
@@ -563,8 +566,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                         x[i] = fast_exp2(fmaf(s_cur[rb][e0 + i], c2, nm[rb]));
                         pin(x[i]);       // computed in this group, not sunk
                     }
-                    l[rb] += (x[0] + x[1]) + (x[2] + x[3]);
-                    pin(l[rb]);
+                    if constexpr (!kSumsRounded) {
+                        l[rb] += (x[0] + x[1]) + (x[2] + x[3]);
+                        pin(l[rb]);
+                    }
                 }
                 if (gi >= 1) {
                     const int u = gi - 1, rb = u >> 2, c = (u >> 1) & 1, half = u & 1;
@@ -580,16 +585,21 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                     p_new[rb][c][2 * half] = a;
                     p_new[rb][c][2 * half + 1] = d;
                     pin(p_new[rb][c]);
-                    if constexpr (Mma<Tin>::kNormRounded && !DROP) {
-                        lr[rb] = Mma<Tin>::add_pair(d, Mma<Tin>::add_pair(a, lr[rb]));
-                        if constexpr (split)
-                            lr[rb] = Mma<Tin>::add_pair(dlo, Mma<Tin>::add_pair(alo, lr[rb]));
-                        pin(lr[rb]);
-                    }
                     if constexpr (split) {
                         p_lo_new[rb][c][2 * half] = alo;
                         p_lo_new[rb][c][2 * half + 1] = dlo;
                         pin(p_lo_new[rb][c]);
+                    }
+                    // the sums read the packed pairs where they now live
+                    // (reading the pack results directly keeps a second copy)
+                    if constexpr (Mma<Tin>::kNormRounded && !DROP) {
+                        lr[rb] = Mma<Tin>::add_pair(p_new[rb][c][2 * half + 1],
+                                                    Mma<Tin>::add_pair(p_new[rb][c][2 * half], lr[rb]));
+                        if constexpr (split)
+                            lr[rb] = Mma<Tin>::add_pair(
+                                p_lo_new[rb][c][2 * half + 1],
+                                Mma<Tin>::add_pair(p_lo_new[rb][c][2 * half], lr[rb]));
+                        pin(lr[rb]);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -880,6 +890,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                     pv_last(std::false_type());
                 }
             }
+        }
+        if constexpr (kSumsRounded) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) l[rb] = lr[rb];
         }
     };
     run_keys(std::false_type(), true);
