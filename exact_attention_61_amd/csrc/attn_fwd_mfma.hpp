@@ -20,12 +20,13 @@
 // overflow is wrong: when a probability passes the 16-bit range (seen as an
 // inf or NaN accumulator for fp16, as an fp32 row sum past the largest bf16
 // for bf16), the work-group redoes the q-tile in a safe form that moves a
-// row's reference whenever a tile's max exceeds it by more than 2^8.  The
-// output is normalised by the fp32 sum of the probabilities as rounded for
-// the PV product (one v_dot2 per pair), so that the rounding of a dominant
-// probability cancels between numerator and denominator.  The log-sum-exp
-// takes the same sum for fp16 (the rounding moves it by less than 2^-11
-// relative) and, for bf16, an fp32 sum of the unrounded probabilities.
+// row's reference whenever a tile's max exceeds it by more than 2^8.  The row
+// sums are taken in fp32 from the unrounded probabilities.  For fp16 inputs
+// they also normalise the output (rounding P to fp16 moves the product by at
+// most 2^-11 relative); for bf16 inputs the output is normalised by the sum
+// of the probabilities as rounded for the PV product (one v_dot2 per pair),
+// so that the rounding of a dominant probability cancels between numerator
+// and denominator.
 //
 // Work decomposition.  A work-group of 4 waves owns BM = 128 query rows of
 // one (batch, head) at a time and walks the keys in tiles of BN = 64 keys.
@@ -423,9 +424,6 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 if (8 * (e >> 2) + (e & 3) > lim) s_cur[rb][e] = -__builtin_inff();
         }
     };
-    // fp16 without dropout: the row sums come from the rounded P only (lr);
-    // l takes their value after the last tile.
-    constexpr bool kSumsRounded = Mma<Tin>::kSumRounded && !DROP;
     // With dropout, bf16 P is split into hi + lo on every tile: the output
     // is normalised by the fp32 sums of the probabilities before dropout,
     // so the rounding of P does not cancel as it does with the rounded sums.
@@ -566,10 +564,8 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                         x[i] = fast_exp2(fmaf(s_cur[rb][e0 + i], c2, nm[rb]));
                         pin(x[i]);       // computed in this group, not sunk
                     }
-                    if constexpr (!kSumsRounded) {
-                        l[rb] += (x[0] + x[1]) + (x[2] + x[3]);
-                        pin(l[rb]);
-                    }
+                    l[rb] += (x[0] + x[1]) + (x[2] + x[3]);
+                    pin(l[rb]);
                 }
                 if (gi >= 1) {
                     const int u = gi - 1, rb = u >> 2, c = (u >> 1) & 1, half = u & 1;
@@ -890,10 +886,6 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                     pv_last(std::false_type());
                 }
             }
-        }
-        if constexpr (kSumsRounded) {
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) l[rb] = lr[rb];
         }
     };
     run_keys(std::false_type(), true);

@@ -19,19 +19,17 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 template <typename T> struct Mma;
 
-// P is rounded to the input type for the PV product.
+// P is rounded to the input type for the PV product; the log-sum-exp always
+// uses the fp32 sum of the unrounded probabilities.  (A sum of the rounded
+// fp16 values, one v_dot2 per pair, would take half the instructions, but
+// its error is not bounded for long rows: a probability in the fp16
+// subnormal range keeps only an absolute precision of 2^-25, and many such
+// terms rounding alike can move the sum by more than the LSE tolerance.)
 //
-// fp16 keeps 11 significant bits: the row sums are taken from the rounded
-// probabilities (one v_dot2 per pair, fp32 accumulation; kSumRounded) and
-// give both the normalisation of O -- so the rounding of a dominant
-// probability cancels -- and the log-sum-exp, which the rounding moves by at
-// most log(1 + 2^-11) < 4.9e-4 (every rounding in the same direction; in
-// practice far less).  Half as many instructions as fp32 adds of the
-// unrounded values.
+// fp16 keeps 11 significant bits: O is normalised by the same fp32 sum, and
+// the rounding of P moves the product by at most 2^-11 relative.
 //
-// bf16 keeps 8, too coarse for the log-sum-exp (2^-8 relative), which uses
-// the fp32 sum of the unrounded probabilities, and too coarse on its own for
-// O in two situations.  (1) One key
+// bf16 keeps 8, too coarse on its own in two situations.  (1) One key
 // dominates a row from a tile after the first: its probability, rounded,
 // would carry ~2^-9 relative error into O.  O is therefore normalised by the
 // sum of the probabilities as rounded (kNormRounded, one v_dot2 per pair),
@@ -50,8 +48,7 @@ template <> struct Mma<f16_t> {
             0, 0, 0);
     }
     static constexpr bool kSplit = false;
-    static constexpr bool kNormRounded = true;
-    static constexpr bool kSumRounded = true;
+    static constexpr bool kNormRounded = false;
     __device__ __forceinline__ static float add_pair(uint32_t pr, float c) {
         const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
         return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pr), one, c, false);
@@ -79,7 +76,6 @@ template <> struct Mma<bf16_t> {
     }
     static constexpr bool kSplit = true;
     static constexpr bool kNormRounded = true;
-    static constexpr bool kSumRounded = false;
     // c + the two packed bf16 values (exact products with 1, fp32 sum)
     __device__ __forceinline__ static float add_pair(uint32_t pr, float c) {
         const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
