@@ -34,12 +34,17 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-file code-generation options.  The d = 64 kernel keeps every MFMA
-# result in architectural VGPRs: its state fits in 256 of them, and results
-# in AGPRs would cost one copy instruction per score to reach the softmax.
+# Per-file code-generation options.  The forward kernels keep every MFMA
+# result in architectural VGPRs: results in AGPRs would cost one copy
+# instruction per score to reach the softmax.  At d = 64 the state fits in
+# 256 VGPRs; at d = 128 (one wave per SIMD, 512 registers) the compiler then
+# uses the AGPRs as spill room, which also removes most scratch spills.
+_VGPR_FORM = ["-mllvm", "--amdgpu-mfma-vgpr-form"]
 FILE_FLAGS = {
-    "attn_fwd_mfma_d64.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
-    "attn_fwd_mfma_drop_d64.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+    "attn_fwd_mfma_d64.hip": _VGPR_FORM,
+    "attn_fwd_mfma_drop_d64.hip": _VGPR_FORM,
+    "attn_fwd_mfma_d128.hip": _VGPR_FORM,
+    "attn_fwd_mfma_drop_d128.hip": _VGPR_FORM,
 }
 
 
