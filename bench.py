@@ -137,6 +137,51 @@ def batch_sizes(steps, batches=5):
     return [steps // nb + (1 if i < steps % nb else 0) for i in range(nb)]
 
 
+def engine_clock_mhz(dev_index):
+    """Peak engine clock the HIP runtime reports (hipDeviceAttributeClockRate,
+    kHz), through the runtime library this process already loaded."""
+    import ctypes
+    try:
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            return None
+        hip = ctypes.CDLL(path)
+        val = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate is entry 5 of hipDeviceAttribute_t
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, int(dev_index)) != 0:
+            return None
+        return val.value / 1000.0
+    except OSError:
+        return None
+
+
+def cold_launch_ms(step, dev, launches=20, flush_mib=512):
+    """Median time of one launch right after writing a buffer larger than the
+    L2 and the 256 MiB fabric cache (the launch's inputs then come from HBM):
+    HIP events around the launch alone, on the current stream."""
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    buf = torch.empty(flush_mib << 20, dtype=torch.uint8, device=dev)
+    times = []
+    for _ in range(launches):
+        buf.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del buf
+    times.sort()
+    return times[len(times) // 2]
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -614,6 +659,8 @@ def main():
         step()
     torch.cuda.synchronize()
     ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
+    # cold launches (inputs evicted from the caches first), for context
+    ms_cold = cold_launch_ms(step, dev)
 
     tflops = flops / (ms * 1e-3) / 1e12
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -674,6 +721,12 @@ def main():
         "ms_per_step_median_batch": round(ms_median, 6),
         "batches": sizes,
         "ms_per_step_eager": round(ms_eager, 6),
+        "cold": {"ms_per_launch_median": round(ms_cold, 6), "launches": 20,
+                 "flush_bytes": 512 << 20,
+                 "value": round(nbytes / (ms_cold * 1e-3) / 1e9, 1) if hbm_bound else
+                 round(flops / (ms_cold * 1e-3) / 1e12, 3),
+                 "note": "one launch after writing 512 MiB (more than L2 + fabric cache); "
+                         "context only, not the headline value"},
         "roofline": roofline,
         "memory": {"peak_allocated_bytes": int(peak),
                    "inputs_outputs_bytes": int(resident),
@@ -682,7 +735,8 @@ def main():
         "cpu_baseline": base,
         "parity": parity,
         "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "gcn_arch": getattr(props, "gcnArchName", None)},
+                   "gcn_arch": getattr(props, "gcnArchName", None),
+                   "peak_engine_clock_mhz": engine_clock_mhz(dev.index or 0)},
     }
     print(json.dumps(rec), flush=True)
 

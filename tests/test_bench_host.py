@@ -100,6 +100,8 @@ def test_bench_json_line_on_gpu(name, bound):
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert rec["cpu_baseline"]["kind"] == "oracle" and rec["cpu_baseline"]["cores"] >= 1
     assert rec["parity"]["pass"]
+    assert rec["cold"]["ms_per_launch_median"] > 0 and rec["cold"]["value"] > 0
+    assert rec["device"]["cus"] >= 1
 
 
 def test_batches_cover_exactly_the_timed_steps():
