@@ -158,6 +158,7 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
 // tensors (packed input) and their counts.
 struct SeqSpan {
     int q0, lq, k0, lk;
+    int tq;                              // packed: all query rows (the LSE row stride)
 };
 
 template <int D, typename Tin, typename Tout, bool CAUSAL, bool DROP>
@@ -192,6 +193,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     };
 
     const int q0 = span.q0, lq_b = span.lq, k0 = span.k0, lk_b = span.lk;
+    const int tq = span.tq;
     const bool packed = p.cu_q != nullptr;
     const int row0 = qtile * kBM;
     if (row0 >= lq_b) return;            // uniform over the work-group
@@ -1011,7 +1013,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                                       ? (r.mu + __log2f(lt)) * 0.69314718055994530942f
                                       : -__builtin_inff();
                 const int64_t li =
-                    packed ? (int64_t)h * p.cu_q[p.batch] + q0 + qrow(rb)
+                    packed ? (int64_t)h * tq + q0 + qrow(rb)
                            : ((int64_t)b * p.hq + h) * p.lq + qrow(rb);
                 p.lse[li] = lse;
             }
@@ -1058,7 +1060,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
 // Span of sequence b of a packed batch.
 __device__ __forceinline__ SeqSpan packed_span(const FwdParams& p, int b) {
     const int q0 = p.cu_q[b], k0 = p.cu_k[b];
-    return SeqSpan{q0, p.cu_q[b + 1] - q0, k0, p.cu_k[b + 1] - k0};
+    return SeqSpan{q0, p.cu_q[b + 1] - q0, k0, p.cu_k[b + 1] - k0, 0};
 }
 
 // Work of a packed non-causal batch of at most 64 sequences, longest key
@@ -1077,7 +1079,7 @@ __device__ __forceinline__ bool packed_item(const FwdParams& p, int& b, int& qti
                                             SeqSpan& span) {
     const int nb = p.batch;
     const int lane = lane_id();
-    SeqSpan mine{0, 0, 0, 0};
+    SeqSpan mine{0, 0, 0, 0, 0};
     if (lane < nb) mine = packed_span(p, lane);
     const int nq = (mine.lq + kBM - 1) / kBM;       // q-tiles of this lane's sequence
     const int ck = (mine.lk + 63) / 64;             // key tiles each of them visits
@@ -1107,8 +1109,10 @@ __device__ __forceinline__ bool packed_item(const FwdParams& p, int& b, int& qti
     const uint64_t own = __builtin_amdgcn_ballot_w64(lane < nb && it >= first && it < first + nq);
     b = (int)__builtin_ctzll(own);
     qtile = it - __builtin_amdgcn_readlane(first, b);
+    // all query rows: the end of the last sequence
+    const int tq = __builtin_amdgcn_readlane(mine.q0 + mine.lq, nb - 1);
     span = SeqSpan{__builtin_amdgcn_readlane(mine.q0, b), __builtin_amdgcn_readlane(mine.lq, b),
-                   __builtin_amdgcn_readlane(mine.k0, b), __builtin_amdgcn_readlane(mine.lk, b)};
+                   __builtin_amdgcn_readlane(mine.k0, b), __builtin_amdgcn_readlane(mine.lk, b), tq};
     return true;
 }
 
@@ -1157,6 +1161,7 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
                 // the longest sequences, whose work-groups are the heaviest
                 t = n_qtiles - 1 - item;
                 span = packed_span(p, b);
+                span.tq = p.cu_q[p.batch];
             }
         }
         if (CAUSAL)
@@ -1174,7 +1179,11 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
             // loop and kept live (spilled) across the whole key loop
             int hh = __builtin_amdgcn_readfirstlane(h), bb = __builtin_amdgcn_readfirstlane(b);
             asm volatile("" : "+s"(hh), "+s"(bb));
-            const SeqSpan span = p.cu_q != nullptr ? packed_span(p, bb) : SeqSpan{0, p.lq, 0, p.lk};
+            SeqSpan span = SeqSpan{0, p.lq, 0, p.lk, 0};
+            if (p.cu_q != nullptr) {
+                span = packed_span(p, bb);
+                span.tq = p.cu_q[p.batch];
+            }
             attend_qtile<D, Tin, Tout, CAUSAL, DROP>(p, tile[it], hh, bb, span);
         }
     } else {
@@ -1197,7 +1206,7 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
             int hh = __builtin_amdgcn_readfirstlane(hb % p.hq);
             int bb = __builtin_amdgcn_readfirstlane(hb / p.hq);
             asm volatile("" : "+s"(hh), "+s"(bb));
-            attend_qtile<D, Tin, Tout, CAUSAL, DROP>(p, t, hh, bb, SeqSpan{0, p.lq, 0, p.lk});
+            attend_qtile<D, Tin, Tout, CAUSAL, DROP>(p, t, hh, bb, SeqSpan{0, p.lq, 0, p.lk, 0});
         }
     }
 }
