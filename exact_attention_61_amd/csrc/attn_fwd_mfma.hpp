@@ -1214,12 +1214,16 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
 template <int D, typename Tin, typename Tout, bool DROP>
 hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
     const int n_qtiles = (p.lq + kBM - 1) / kBM;
-    // causal q-tile order: with two resident work-groups per CU, grid
-    // halves heaviest-first and lightest-first (2); with one, heaviest first
-    // (0: measured 1 % faster than q-tile pairs in one work-group at d = 128)
+    // causal q-tile order: with two resident work-groups per CU and a grid
+    // that the device holds at once, grid halves heaviest-first and
+    // lightest-first (2: the CU's pair sums to about the same work); with a
+    // larger grid or one work-group per CU, heaviest first (0: the
+    // dispatcher then balances as slots free up; measured 5 % faster at
+    // B4 H32 N1024, and 1 % faster than q-tile pairs at d = 128)
+    const int64_t n_wg = (int64_t)p.hq * p.batch * n_qtiles;
     const int pair = !p.causal ? 0
                      : p.causal_pairs >= 0 ? p.causal_pairs
-                     : (Layout<D>::WG_PER_CU == 2 ? 2 : 0);
+                     : (Layout<D>::WG_PER_CU == 2 && n_wg <= 2 * (int64_t)p.n_cu ? 2 : 0);
     const int items = (p.causal && pair == 1) ? (n_qtiles + 1) / 2 : n_qtiles;
     // grid limits (y and z below 2^16) are checked by the caller
     const dim3 grid((unsigned)p.hq, (unsigned)p.batch, (unsigned)items);
