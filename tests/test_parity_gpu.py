@@ -465,6 +465,18 @@ def test_causal_tile_orders(order, b, h, lq, lk, d, dtype):
     dense_case(b, h, h, lq, lk, d, dtype, True, causal_order=order)
 
 
+@pytest.mark.parametrize("b,h,lq,dtype", [
+    (1, 64, 1024, F16),     # 512 work-groups: the device holds the grid, grid-halves order
+    (1, 65, 1024, BF16),    # 520: more than the device holds, heaviest first
+    (2, 33, 1000, F16),     # 528 work-groups, a partial last q-tile
+])
+def test_causal_default_order_around_the_device_size(b, h, lq, dtype):
+    """d = 64 causal picks its q-tile order by whether the device holds the
+    whole grid at once; both sides of that boundary against the oracle."""
+    note(f"causal default order b{b} h{h} lq{lq} {dtype}")
+    dense_case(b, h, h, lq, lq, 64, dtype, True)
+
+
 @pytest.mark.parametrize("b,hq,hkv,lq,lk,causal", [
     (1, 32, 8, 1024, 1024, True),     # more q-tiles than resident work-groups
     (2, 7, 7, 700, 900, False),       # rounds that do not fill the grid
