@@ -193,6 +193,8 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
     };
 
     const int q0 = span.q0, lq_b = span.lq, k0 = span.k0, lk_b = span.lk;
+    // packed: the LSE row stride (the dropout kernels, short of registers,
+    // load it in the epilogue instead of keeping it live)
     const int tq = span.tq;
     const bool packed = p.cu_q != nullptr;
     const int row0 = qtile * kBM;
@@ -1013,7 +1015,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                                       ? (r.mu + __log2f(lt)) * 0.69314718055994530942f
                                       : -__builtin_inff();
                 const int64_t li =
-                    packed ? (int64_t)h * tq + q0 + qrow(rb)
+                    packed ? (int64_t)h * (DROP ? p.cu_q[p.batch] : tq) + q0 + qrow(rb)
                            : ((int64_t)b * p.hq + h) * p.lq + qrow(rb);
                 p.lse[li] = lse;
             }
