@@ -161,15 +161,19 @@ def engine_clock_mhz(dev_index):
 
 
 def cold_launch_ms(step, dev, launches=20, flush_mib=512):
-    """Median time of one launch right after writing a buffer larger than the
-    L2 and the 256 MiB fabric cache (the launch's inputs then come from HBM):
-    HIP events around the launch alone, on the current stream."""
+    """Median time of one launch right after reading a buffer larger than the
+    L2 and the 256 MiB fabric cache (the launch's inputs then come from HBM,
+    and the caches hold clean lines of that buffer, so no write-back competes
+    with the launch): HIP events around the launch alone, on the current
+    stream."""
     import torch
     stream = torch.cuda.current_stream(dev)
-    buf = torch.empty(flush_mib << 20, dtype=torch.uint8, device=dev)
+    buf = torch.ones(flush_mib << 18, dtype=torch.float32, device=dev)
+    buf.max()                            # the first pass leaves its writes behind
+    torch.cuda.synchronize()
     times = []
     for _ in range(launches):
-        buf.fill_(1)
+        buf.max()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -725,7 +729,7 @@ def main():
                  "flush_bytes": 512 << 20,
                  "value": round(nbytes / (ms_cold * 1e-3) / 1e9, 1) if hbm_bound else
                  round(flops / (ms_cold * 1e-3) / 1e12, 3),
-                 "note": "one launch after writing 512 MiB (more than L2 + fabric cache); "
+                 "note": "one launch after reading 512 MiB (more than L2 + fabric cache); "
                          "context only, not the headline value"},
         "roofline": roofline,
         "memory": {"peak_allocated_bytes": int(peak),
