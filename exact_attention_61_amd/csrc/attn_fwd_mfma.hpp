@@ -502,7 +502,11 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         constexpr int NPVT = split ? 2 * NPV : NPV;   // with the lo products
         constexpr int NQK = next ? 2 * NKS : 0;
         constexpr int NM = NPVT + NQK;
-        constexpr int kGroups = safe ? 13 : 9;
+        // d = 128 runs one wave per SIMD, whose vector work overlaps the
+        // matrix products better in smaller pieces: its short form gives
+        // the exponentials and the packing of each part groups of their own
+        constexpr bool kFine = D == 128 && !safe;
+        constexpr int kGroups = safe ? 13 : (kFine ? 17 : 9);
         // O += P(j-1) V(j-1) first: its fragments were read in the previous
         // step.  S(j+1) = Q K(j+1)^T after it, by when the K(j+1) fragments
         // read at the start of this step have landed.
@@ -553,16 +557,23 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         const auto rsrc = tile_rsrc(dma_kt);
         if constexpr (!safe) {
             // Part u (0..7) = scores 4 * (u & 3) .. +3 of row block u >> 2:
-            // group g exponentiates and sums part g and rounds part g - 1.
+            // group g exponentiates and sums part g and rounds part g - 1
+            // (kFine: group 2u exponentiates part u, group 2u + 1 rounds it).
             // The row sums go straight into l (fp32) and, for bf16, lr.
             float pe[2][4];              // probabilities of the last two parts
             uint32_t dw[4];              // dropout words of the current part pair
 #pragma unroll
             for (int gi = 0; gi < kGroups; ++gi) {
                 vread_at(gi);
-                if (gi < 8) {
-                    const int rb = gi >> 2, e0 = 4 * (gi & 3);
-                    float* x = pe[gi & 1];
+                // part of the exponentials in this group (-1: none), and
+                // part of the packing (-1: none)
+                const int ex = kFine ? ((gi & 1) == 0 && gi / 2 < 8 ? gi / 2 : -1)
+                                     : (gi < 8 ? gi : -1);
+                const int pk = kFine ? ((gi & 1) == 1 ? (gi - 1) / 2 : -1)
+                                     : (gi >= 1 ? gi - 1 : -1);
+                if (ex >= 0) {
+                    const int rb = ex >> 2, e0 = 4 * (ex & 3);
+                    float* x = pe[ex & 1];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         x[i] = fast_exp2(fmaf(s_cur[rb][e0 + i], c2, nm[rb]));
@@ -571,8 +582,8 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                     l[rb] += (x[0] + x[1]) + (x[2] + x[3]);
                     pin(l[rb]);
                 }
-                if (gi >= 1) {
-                    const int u = gi - 1, rb = u >> 2, c = (u >> 1) & 1, half = u & 1;
+                if (pk >= 0) {
+                    const int u = pk, rb = u >> 2, c = (u >> 1) & 1, half = u & 1;
                     float (&x)[4] = pe[u & 1];
                     if constexpr (DROP) {
                         if ((u & 1) == 0) drop_words(j, rb, u & 3, dw);
