@@ -29,9 +29,9 @@ notes of the repository):
 * LSE is the natural log of sum_j exp(scale * q_i . k_j) over visible keys;
 * query head h uses KV head floor(h / G), G = Hq / Hkv (contiguous groups).
 
-Parity unpinned: the bottom-right causal rule for Lq != Lk is checked only
-against restatements of the same rule (the scalar brute force and the
-closed-form key counts); the pages fix no example of it.
+The bottom-right causal rule for Lq != Lk is pinned to a library: torch's
+lower-right causal bias with its CPU float64 scaled-dot-product attention
+(the pages fix no example of it).
 
 Layouts: dense tensors are [B, H, L, d]; packed variable-length tensors are
 [T, H, d] with cu_seqlens int arrays of length B + 1 (sequence b owns rows

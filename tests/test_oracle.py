@@ -313,6 +313,46 @@ def test_matches_torch_sdpa_and_logsumexp(causal, shape):
     assert np.allclose(lse, logsumexp(s, axis=-1), atol=1e-12, rtol=0)
 
 
+@pytest.mark.parametrize("lq,lk", [(5, 13), (17, 40), (13, 5), (40, 17), (1, 9), (9, 1)])
+def test_bottom_right_causal_matches_torch_lower_right_bias(lq, lk):
+    """Causal with Lq != Lk against torch's lower-right causal bias (the
+    library's own definition of that alignment), CPU float64 SDPA: O on
+    every row that sees a key, and the LSE from the library's probabilities
+    (SDPA with V = identity returns P; LSE_i = s_ij - log P_ij for any visible
+    j).  Rows that see no key (Lq > Lk): the library returns NaN or zeros
+    there (depending on the version), the oracle O = 0 and LSE = -inf (its
+    own reading)."""
+    from torch.nn.attention.bias import causal_lower_right
+    import warnings
+    rng = _rng(100 + lq * 7 + lk)
+    d, scale = 8, 0.35
+    q = rng.standard_normal((1, 2, lq, d))
+    k = rng.standard_normal((1, 2, lk, d))
+    v = rng.standard_normal((1, 2, lk, d))
+    o, lse = oracle.attention(q, k, v, scale=scale, causal=True)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")          # the bias warns about NaN rows
+        bias = causal_lower_right(lq, lk)
+        want = torch.nn.functional.scaled_dot_product_attention(
+            t(q), t(k), t(v), attn_mask=bias, scale=scale).numpy()
+        eye = np.broadcast_to(np.eye(lk), (1, 2, lk, lk))
+        prob = torch.nn.functional.scaled_dot_product_attention(
+            t(q), t(k), t(eye), attn_mask=bias, scale=scale).numpy()
+    seen = np.nan_to_num(prob).sum(axis=-1) > 0.5   # rows whose probabilities sum to 1
+    assert np.allclose(o[seen], want[seen], atol=1e-12, rtol=0)
+    assert np.all(o[~seen] == 0.0) and np.all(lse[~seen] == -np.inf)
+    assert seen.all() or lq > lk
+    s = scale * np.einsum("bhid,bhjd->bhij", q, k)
+    for b, h, i in zip(*np.nonzero(seen)):
+        j = int(np.argmax(prob[b, h, i]))
+        assert abs(lse[b, h, i] - (s[b, h, i, j] - math.log(prob[b, h, i, j]))) < 1e-12
+    # the visible keys are exactly where the library's probabilities are > 0
+    rows, cols = np.nonzero(prob[0, 0] > 0)
+    assert np.all(cols <= rows + lk - lq)
+    assert len(rows) == sum(max(0, min(lk, i + lk - lq + 1)) for i in range(lq))
+
+
 def test_varlen_equals_per_sequence_and_padded_mask():
     """Packed sequences == one dense call per sequence == padded batch with a
     key padding mask (True = keep), on the valid query rows."""
