@@ -502,11 +502,10 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         constexpr int NPVT = split ? 2 * NPV : NPV;   // with the lo products
         constexpr int NQK = next ? 2 * NKS : 0;
         constexpr int NM = NPVT + NQK;
-        // d = 128 runs one wave per SIMD, whose vector work overlaps the
-        // matrix products better in smaller pieces: its short form gives
-        // the exponentials and the packing of each part groups of their own
-        constexpr bool kFine = D == 128 && !safe;
-        constexpr int kGroups = safe ? 13 : (kFine ? 17 : 9);
+        // The vector work overlaps the matrix products better in smaller
+        // pieces (about 2 products per group): the short form gives the
+        // exponentials and the packing of each part groups of their own.
+        constexpr int kGroups = safe ? 13 : 17;
         // O += P(j-1) V(j-1) first: its fragments were read in the previous
         // step.  S(j+1) = Q K(j+1)^T after it, by when the K(j+1) fragments
         // read at the start of this step have landed.
@@ -557,20 +556,17 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         const auto rsrc = tile_rsrc(dma_kt);
         if constexpr (!safe) {
             // Part u (0..7) = scores 4 * (u & 3) .. +3 of row block u >> 2:
-            // group g exponentiates and sums part g and rounds part g - 1
-            // (kFine: group 2u exponentiates part u, group 2u + 1 rounds it).
+            // group 2u exponentiates and sums part u, group 2u + 1 rounds it.
             // The row sums go straight into l (fp32) and, for bf16, lr.
-            float pe[2][4];              // probabilities of the last two parts
+            float pe[2][4];              // probabilities of the current part
             uint32_t dw[4];              // dropout words of the current part pair
 #pragma unroll
             for (int gi = 0; gi < kGroups; ++gi) {
                 vread_at(gi);
                 // part of the exponentials in this group (-1: none), and
                 // part of the packing (-1: none)
-                const int ex = kFine ? ((gi & 1) == 0 && gi / 2 < 8 ? gi / 2 : -1)
-                                     : (gi < 8 ? gi : -1);
-                const int pk = kFine ? ((gi & 1) == 1 ? (gi - 1) / 2 : -1)
-                                     : (gi >= 1 ? gi - 1 : -1);
+                const int ex = (gi & 1) == 0 && gi / 2 < 8 ? gi / 2 : -1;
+                const int pk = (gi & 1) == 1 ? (gi - 1) / 2 : -1;
                 if (ex >= 0) {
                     const int rb = ex >> 2, e0 = 4 * (ex & 3);
                     float* x = pe[ex & 1];
