@@ -534,7 +534,11 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         auto vread_at = [&](int gi) {
             if (gi == kGroupV) read_v(v_next);
         };
-        if constexpr (masked_tile) mask_cur(j);
+        // d = 64: the short form masks each part in the group that
+        // exponentiates it (at d = 128 that made the compiler's register
+        // allocation of the whole kernel worse: L8192 +17 %)
+        constexpr bool kMaskParts = D == 64 && !safe;
+        if constexpr (masked_tile && !kMaskParts) mask_cur(j);
         u32x4_t p_new[2][2];             // this tile's P; p_prev stays for PV
         u32x4_t p_lo_new[2][2];          // its low part (split only)
         // pack a pair of probabilities; with the split also their low parts
@@ -569,6 +573,12 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
                 const int pk = (gi & 1) == 1 ? (gi - 1) / 2 : -1;
                 if (ex >= 0) {
                     const int rb = ex >> 2, e0 = 4 * (ex & 3);
+                    if constexpr (masked_tile && kMaskParts) {
+                        const int lim = last_key(rb) - (j * BN + 32 * kq + 4 * hi);
+#pragma unroll
+                        for (int e = e0; e < e0 + 4; ++e)
+                            if (8 * (e >> 2) + (e & 3) > lim) s_cur[rb][e] = -__builtin_inff();
+                    }
                     float* x = pe[ex & 1];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
