@@ -505,7 +505,11 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         // The vector work overlaps the matrix products better in smaller
         // pieces (about 2 products per group): the short form gives the
         // exponentials and the packing of each part groups of their own.
-        constexpr int kGroups = safe ? 13 : 17;
+        // The bf16 dropout kernel at d = 64 keeps 9 groups (exponentials of
+        // a part and packing of the one before in one group): there the
+        // finer schedule lengthens live ranges into more spills.
+        constexpr bool kFine = !(D == 64 && DROP && Mma<Tin>::kSplit);
+        constexpr int kGroups = safe ? 13 : (kFine ? 17 : 9);
         // O += P(j-1) V(j-1) first: its fragments were read in the previous
         // step.  S(j+1) = Q K(j+1)^T after it, by when the K(j+1) fragments
         // read at the start of this step have landed.
@@ -537,7 +541,7 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         // d = 64: the short form masks each part in the group that
         // exponentiates it (at d = 128 that made the compiler's register
         // allocation of the whole kernel worse: L8192 +17 %)
-        constexpr bool kMaskParts = D == 64 && !safe;
+        constexpr bool kMaskParts = D == 64 && !safe && kFine;
         if constexpr (masked_tile && !kMaskParts) mask_cur(j);
         u32x4_t p_new[2][2];             // this tile's P; p_prev stays for PV
         u32x4_t p_lo_new[2][2];          // its low part (split only)
@@ -560,17 +564,20 @@ __device__ __forceinline__ void attend_qtile(const FwdParams& p, int qtile,
         const auto rsrc = tile_rsrc(dma_kt);
         if constexpr (!safe) {
             // Part u (0..7) = scores 4 * (u & 3) .. +3 of row block u >> 2:
-            // group 2u exponentiates and sums part u, group 2u + 1 rounds it.
+            // group 2u exponentiates and sums part u, group 2u + 1 rounds it
+            // (9 groups: group g exponentiates part g and rounds part g - 1).
             // The row sums go straight into l (fp32) and, for bf16, lr.
-            float pe[2][4];              // probabilities of the current part
+            float pe[2][4];              // probabilities of the last two parts
             uint32_t dw[4];              // dropout words of the current part pair
 #pragma unroll
             for (int gi = 0; gi < kGroups; ++gi) {
                 vread_at(gi);
                 // part of the exponentials in this group (-1: none), and
                 // part of the packing (-1: none)
-                const int ex = (gi & 1) == 0 && gi / 2 < 8 ? gi / 2 : -1;
-                const int pk = (gi & 1) == 1 ? (gi - 1) / 2 : -1;
+                const int ex = kFine ? ((gi & 1) == 0 && gi / 2 < 8 ? gi / 2 : -1)
+                                     : (gi < 8 ? gi : -1);
+                const int pk = kFine ? ((gi & 1) == 1 ? (gi - 1) / 2 : -1)
+                                     : (gi >= 1 ? gi - 1 : -1);
                 if (ex >= 0) {
                     const int rb = ex >> 2, e0 = 4 * (ex & 3);
                     if constexpr (masked_tile && kMaskParts) {
