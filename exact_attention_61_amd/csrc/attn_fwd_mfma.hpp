@@ -1149,10 +1149,9 @@ __device__ __forceinline__ bool packed_item(const FwdParams& p, int& b, int& qti
 //   non-causal: item = q-tile; packed batches of at most 64 sequences are
 //     ranked by packed_item, larger ones take q-tile n-1-item.
 //   causal: q-tiles heaviest first; with `pair` 1 item t covers q-tiles
-//     n-1-t and t one after the other; with `pair` 2 the first half of the
-//     items goes heaviest-first and the second half lightest-first, so that
-//     the two work-groups a CU holds (dispatched half a grid apart) sum to
-//     about the same work everywhere.
+//     n-1-t and t one after the other; with `pair` 2 the second round of
+//     n_cu work-groups runs lightest first, so that the two work-groups a
+//     CU holds (dispatched n_cu apart) sum to about the same work.
 // Work-group modes: one q-tile, the causal pair (n-1-t, t), or resident
 // work-groups looping over ranked q-tiles.
 enum { kModeOne = 0, kModePairs = 1, kModeResident = 2 };
@@ -1170,7 +1169,32 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
     const int item = (int)blockIdx.z;
     if constexpr (MODE == kModeOne) {
         // one q-tile per work-group: a straight-line body
-        int t = item;
+        int it = item;
+        // (d = 128 keeps the halves order below: this remap, even untaken,
+        // changes the register allocation of its saturated kernel)
+        if (D == 64 && CAUSAL && pair == 2) {
+            // Causal order 2.  In grid order (head fastest, then batch, then
+            // item) the work-groups rank heaviest first.  The first n_cu take
+            // one slot on every CU; the dispatcher deals the next ones to
+            // the second slots in the same CU order, so ranks lo .. hi-1 of
+            // that round are taken in reverse -- lightest first -- and each
+            // CU's pair sums to about the same work.  The reversal moves
+            // blocks of 8 work-groups, which keeps every rank on the XCD
+            // (grid index mod 8) of its own position.
+            const uint32_t gx = gridDim.x, cols = gx * gridDim.y;
+            const uint32_t lo = (uint32_t)p.n_cu;
+            const uint32_t hi = min(cols * gridDim.z, 2u * lo);   // grid below 2^31 (launcher)
+            const uint32_t blocks = hi > lo ? (hi - lo) >> 3 : 0u;
+            const uint32_t r = (uint32_t)it * cols + (uint32_t)b * gx + (uint32_t)h;
+            if (r >= lo && r - lo < 8u * blocks) {
+                const uint32_t rr = lo + 8u * (blocks - 1u - ((r - lo) >> 3)) + ((r - lo) & 7u);
+                it = (int)(rr / cols);
+                const uint32_t col = rr - (uint32_t)it * cols;
+                b = (int)(col / gx);
+                h = (int)(col - (uint32_t)b * gx);
+            }
+        }
+        int t = it;
         SeqSpan span{0, p.lq, 0, p.lk};
         // Grouped heads: the dispatcher deals consecutive work-groups to the
         // 8 XCDs in turn, so with hq a multiple of 8 the work-group of grid
@@ -1185,14 +1209,21 @@ __global__ __launch_bounds__(Layout<D>::THREADS, Layout<D>::WG_PER_CU) void attn
             } else {
                 // highest q-tile index first: those q-tiles exist only for
                 // the longest sequences, whose work-groups are the heaviest
-                t = n_qtiles - 1 - item;
+                t = n_qtiles - 1 - it;
                 span = packed_span(p, b);
                 span.tq = p.cu_q[p.batch];
             }
         }
-        if (CAUSAL)
-            t = pair == 2 ? (item < n_qtiles / 2 ? n_qtiles - 1 - item : item - n_qtiles / 2)
-                          : n_qtiles - 1 - item;
+        if (CAUSAL) {
+            if constexpr (D == 64) {
+                t = n_qtiles - 1 - it;
+            } else {
+                // order 2 at d = 128: the first half of the items heaviest
+                // first, the second half lightest first
+                t = pair == 2 ? (item < n_qtiles / 2 ? n_qtiles - 1 - item : item - n_qtiles / 2)
+                              : n_qtiles - 1 - item;
+            }
+        }
         attend_qtile<D, Tin, Tout, CAUSAL, DROP>(p, t, h, b, span);
     } else if constexpr (MODE == kModePairs) {
         // causal, q-tiles n-1-item and item one after the other
@@ -1241,15 +1272,16 @@ template <int D, typename Tin, typename Tout, bool DROP>
 hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
     const int n_qtiles = (p.lq + kBM - 1) / kBM;
     // causal q-tile order: with two resident work-groups per CU and a grid
-    // that the device holds at once, grid halves heaviest-first and
-    // lightest-first (2: the CU's pair sums to about the same work); with a
-    // larger grid or one work-group per CU, heaviest first (0: the
+    // that the device holds at once, heaviest first with the second round
+    // of n_cu reversed (2: the CU's pair sums to about the same work); with
+    // a larger grid or one work-group per CU, heaviest first (0: the
     // dispatcher then balances as slots free up; measured 5 % faster at
     // B4 H32 N1024, and 1 % faster than q-tile pairs at d = 128)
     const int64_t n_wg = (int64_t)p.hq * p.batch * n_qtiles;
-    const int pair = !p.causal ? 0
-                     : p.causal_pairs >= 0 ? p.causal_pairs
-                     : (Layout<D>::WG_PER_CU == 2 && n_wg <= 2 * (int64_t)p.n_cu ? 2 : 0);
+    int pair = !p.causal ? 0
+               : p.causal_pairs >= 0 ? p.causal_pairs
+               : (Layout<D>::WG_PER_CU == 2 && n_wg <= 2 * (int64_t)p.n_cu ? 2 : 0);
+    if (pair == 2 && n_wg >= (int64_t)1 << 31) pair = 0;   // order 2 ranks in 32 bits
     const int items = (p.causal && pair == 1) ? (n_qtiles + 1) / 2 : n_qtiles;
     // grid limits (y and z below 2^16) are checked by the caller
     const dim3 grid((unsigned)p.hq, (unsigned)p.batch, (unsigned)items);

@@ -170,8 +170,11 @@ typedef enum mi_attn_kernel {
  *               -1 the library's default for the head dimension;
  *                0 one query tile per work-group, heaviest first;
  *                1 query tiles t and n-1-t in one work-group;
- *                2 one query tile per work-group, the first half of the grid
- *                  heaviest first and the second half lightest first;
+ *                2 one query tile per work-group; head_dim 64: heaviest
+ *                  first, except that the second round of as many
+ *                  work-groups as the device has CUs runs lightest first
+ *                  (in blocks of 8); head_dim 128: the first half of the
+ *                  grid heaviest first and the second half lightest first;
  *                3 (head_dim 128, dense inputs, causal or not) resident
  *                  work-groups, one per slot the device holds at once,
  *                  each looping over query tiles ranked heaviest first and
