@@ -335,6 +335,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void attn_decode_kernel(DecParams p
 // rule of the online softmax, as across work-groups).  Lane j holds columns
 // j, j + 64, ... of the row.
 constexpr int kCombineRows = 4;          // rows (waves) per work-group
+constexpr int kCombineUnrolled = 8;      // split counts merged with all loads up front
 
 template <int D, typename Tout>
 __global__ __launch_bounds__(64 * kCombineRows) void attn_decode_combine_kernel(DecParams p) {
@@ -348,19 +349,51 @@ __global__ __launch_bounds__(64 * kCombineRows) void attn_decode_combine_kernel(
     const int hq = (int)(bh % p.hq), b = (int)(bh / p.hq);
     const float* pm = p.part_ml + rid * p.splits * 2;
     const float* po = p.part_o + rid * p.splits * D + lane;
-    float M = -__builtin_inff();
-    for (int s = 0; s < p.splits; ++s) M = max2(M, pm[2 * s]);
-    const float mu = M == -__builtin_inff() ? 0.0f : M;
-    float L = 0.0f;
+    float M = -__builtin_inff(), L = 0.0f;
     float o[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) o[c] = 0.0f;
-    for (int s = 0; s < p.splits; ++s) {
-        const float w = pm[2 * s + 1] * fast_exp2(pm[2 * s] - mu);
-        L += w;
+    if (p.splits <= kCombineUnrolled) {
+        // every load of the row issued at once (the partials come from
+        // other XCDs' writes, a round trip to the fabric each): one round
+        // trip instead of one for (m, l) and another for the outputs
+        float ms[kCombineUnrolled], ls[kCombineUnrolled], os[kCombineUnrolled][CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) o[c] = fmaf(po[s * D + 64 * c], w, o[c]);
+        for (int s = 0; s < kCombineUnrolled; ++s) {
+            ms[s] = -__builtin_inff();
+            ls[s] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) os[s][c] = 0.0f;
+            if (s < p.splits) {
+                ms[s] = pm[2 * s];
+                ls[s] = pm[2 * s + 1];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) os[s][c] = po[s * D + 64 * c];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < kCombineUnrolled; ++s) M = max2(M, ms[s]);
+        const float mu = M == -__builtin_inff() ? 0.0f : M;
+#pragma unroll
+        for (int s = 0; s < kCombineUnrolled; ++s) {
+            if (s < p.splits) {
+                const float w = ls[s] * fast_exp2(ms[s] - mu);
+                L += w;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) o[c] = fmaf(os[s][c], w, o[c]);
+            }
+        }
+    } else {
+        for (int s = 0; s < p.splits; ++s) M = max2(M, pm[2 * s]);
+        const float mu = M == -__builtin_inff() ? 0.0f : M;
+        for (int s = 0; s < p.splits; ++s) {
+            const float w = pm[2 * s + 1] * fast_exp2(pm[2 * s] - mu);
+            L += w;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) o[c] = fmaf(po[s * D + 64 * c], w, o[c]);
+        }
     }
+    const float mu = M == -__builtin_inff() ? 0.0f : M;
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const int64_t orow = (int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + (int64_t)pos * p.o_sr;
 #pragma unroll
